@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of fused exact attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch: fa_fwd (O, LSE)
+followed by fa_bwd (dQ, dK, dV) on the fwd+bwd workload (B=2, H=16, N=2048,
+d=128, causal; the only workload with a backward pass). ``--workload 1..4``
+times the forward-only workloads instead (the causal d=128 long-sequence
+forwards are 3 and 4).
+
+Prints ONE JSON line. ``value`` is algorithmic TFLOP/s over the timed steps
+(forward 4*B*H*N^2*d, backward 10*B*H*N^2*d, each halved when causal) with
+inputs resident in HBM. ``roofline`` describes the dominant launch, timed with
+HIP events on the stream the kernels run on. ``cpu_baseline`` times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOP/s (bf16, d=128) and % of MI355X bf16 MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time budget of the oracle sample")
+    p.add_argument("--copy-calib-mib", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def fwd_bytes(w):
+    n = w.B * w.H * w.N
+    return 4 * n * w.d * 2 + 4 * n
+
+
+def bwd_bytes(w):
+    n = w.B * w.H * w.N
+    return 5 * n * w.d * 2 + 4 * n + 8 * n + 3 * n * w.d * 2
+
+
+def cpu_baseline(w, inp, budget_s):
+    """Time the oracle (as it stands) on a bounded sample of heads."""
+    import numpy as np
+    import oracle
+    from exact_io_aware_12_amd.inputs import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(x.get("num_threads", 1)) for x in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, flops, t_total = 0, 0.0, 0.0
+    per_head_fwd = w.fwd_flops() / len(heads)
+    per_head_bwd = w.bwd_flops() / len(heads) if w.backward else 0.0
+    for b, h in heads:
+        q = bf16_bits_to_f64(inp.q[b, h]); k = bf16_bits_to_f64(inp.k[b, h])
+        v = bf16_bits_to_f64(inp.v[b, h])
+        t0 = time.perf_counter()
+        oracle.attention_fwd(q, k, v, w.scale, w.causal)
+        if w.backward:
+            oracle.attention_bwd(q, k, v, bf16_bits_to_f64(inp.do[b, h]), w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+        flops += per_head_fwd + per_head_bwd
+        if t_total >= budget_s:
+            break
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} heads, {'fwd+bwd' if w.backward else 'fwd'} in fp64 "
+                  f"(numpy/OpenBLAS), {t_total:.1f} s",
+        "seconds_per_step_extrapolated": t_total / done * len(heads),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(attention shards by head with no exchange; see the design notes). "
+              f"Asked for --gpus {args.gpus} (WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from exact_io_aware_12_amd import fa
+    from exact_io_aware_12_amd import inputs as fi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.library()
+    dev = torch.device("cuda:0")
+    w = fi.WORKLOADS[args.workload]
+    inp = fi.make_inputs(args.workload)
+
+    def gpu(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = gpu(inp.q), gpu(inp.k), gpu(inp.v)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), device=dev, dtype=torch.float32)
+    if w.backward:
+        do = gpu(inp.do)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), device=dev,
+                         dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        if w.backward:
+            fa.bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, workspace=ws,
+                   dq=dq, dk=dk, dv=dv)
+            if ev is not None:
+                ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in events] if w.backward else [0.0] * args.steps
+    ms_step = wall * 1e3 / args.steps
+    flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    f_avg = sum(fwd_ms) / len(fwd_ms)
+    b_avg = sum(bwd_ms) / len(bwd_ms)
+    fwd_tf = w.fwd_flops() / (f_avg * 1e-3) / 1e12
+    bwd_tf = (w.bwd_flops() / (b_avg * 1e-3) / 1e12) if w.backward else None
+    if w.backward and b_avg > f_avg:
+        dom = {"launch": "fa_bwd (kernels fa_bwd_pre, fa_bwd_main, fa_bwd_dq back to back)",
+               "achieved": bwd_tf, "avg_ms": b_avg}
+    else:
+        dom = {"launch": "fa_fwd (kernel fa_fwd_kernel)", "achieved": fwd_tf, "avg_ms": f_avg}
+    roofline = {"bound": "mfma", "achieved": round(dom["achieved"], 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": dom["launch"], "avg_launch_ms": round(dom["avg_ms"], 4)}
+
+    if args.copy_calib_mib > 0:
+        src = torch.empty(args.copy_calib_mib * 2 ** 20, device=dev, dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "key_scale": w.key_scale,
+                   "pass": "fwd+bwd" if w.backward else "fwd"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"avg_ms": round(f_avg, 4), "min_ms": round(min(fwd_ms), 4),
+                "tflops": round(fwd_tf, 2),
+                "hbm_alg_GBs": round(fwd_bytes(w) / (f_avg * 1e-3) / 1e9, 1)},
+        "roofline": roofline,
+    }
+    if w.backward:
+        rec["bwd"] = {"avg_ms": round(b_avg, 4), "min_ms": round(min(bwd_ms), 4),
+                      "tflops": round(bwd_tf, 2),
+                      "hbm_alg_GBs": round(bwd_bytes(w) / (b_avg * 1e-3) / 1e9, 1)}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,57 @@
+"""Build libfa355.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+
+Usage: ``python -m exact_io_aware_12_amd.build`` (or ``__graft_entry__.build()``).
+Always recompiles. Needs only hipcc; no GPU is touched.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libfa355.so")
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+# Packed fp32 VALU instructions are kept out of every kernel.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-fvisibility=hidden",
+          "-Wno-unused-command-line-argument"]
+
+
+def _compile(src: str, obj: str, extra: list[str]) -> None:
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    noise = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln]
+    if any("warning" in ln for ln in noise):
+        sys.stderr.write("\n".join(noise) + "\n")
+
+
+def build(extra: list[str] | None = None) -> str:
+    extra = list(extra or [])
+    tmp = tempfile.mkdtemp(prefix="fa355_build_")
+    try:
+        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            list(ex.map(lambda a: _compile(a[0], a[1], extra), zip(SOURCES, objs)))
+        out_tmp = LIB + ".tmp"
+        cmd = [HIPCC, *COMMON, "-shared", *objs, "-o", out_tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(out_tmp, LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(sys.argv[1:]))

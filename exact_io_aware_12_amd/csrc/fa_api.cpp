@@ -1,0 +1,102 @@
+// C ABI of libfa355.so: argument validation and dispatch to the HIP kernels.
+//
+// Every check runs before the first HIP call, so an invalid call returns an
+// error code without launching anything (and works on a machine with no GPU).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa355.h"
+
+namespace fa {
+hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        uint16_t* o, float* lse, int BH, int N, int d, float scale,
+                        bool causal, hipStream_t stream);
+hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* o, const uint16_t* dout, const float* lse,
+                        uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dqacc, float* dvec,
+                        int BH, int N, int d, float scale, bool causal, hipStream_t stream);
+}  // namespace fa
+
+namespace {
+
+constexpr int64_t kMaxElems = 2147483647;  // 2^31 - 1
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  const int64_t elems = (int64_t)B * H * N * d;
+  if (elems > kMaxElems) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != FA_OK) return rc;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  hipError_t e = fa::fwd_dispatch(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B * H, N, d, scale,
+      causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+           void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != FA_OK) return rc;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * N;
+  float* dqacc = static_cast<float*>(workspace);
+  float* dvec = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         round256(rows * d * sizeof(float)));
+  hipError_t e = fa::bwd_dispatch(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
+      static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dqacc, dvec, B * H, N, d, scale,
+      causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape: B, H and N must be >= 1 and B*H*N*d < 2^31";
+    case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
+    case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "backward workspace is NULL or too small";
+    case FA_ERR_HIP: return "the HIP runtime reported a launch error";
+    default: return "unknown fa355 error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Device-side building blocks shared by the forward and backward kernels of
+// the fused exact attention library (gfx950 / CDNA4 only).
+//
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16, one
+// wave64): for D(32x32) += A(32x16) * B(16x32)
+//   * A operand: lane l holds 8 bf16 of row (l % 32), k-slots 8*(l/32)+0..7;
+//   * B operand: lane l holds 8 bf16 of column (l % 32), the same k-slots;
+//   * accumulator: lane l, register i holds D[row][col] with col = l % 32 and
+//     row = 8*(i/4) + 4*(l/32) + (i%4).
+// A and B see the k-slots in the same order, so any consistent assignment of
+// the contraction index to (half, slot) gives the same sum; the kernels use
+// this to feed accumulator registers back in as an operand without moving
+// them across lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) (v_log_f32).
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane (l ^ 32): the other half of the wave.
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// Two fp32 -> two bf16 (round to nearest even), packed in one dword.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2 b = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// Eight fp32 -> a bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
+                                              float a4, float a5, float a6, float a7) {
+  u32x4 u = {pack_bf16x2(a0, a1), pack_bf16x2(a2, a3), pack_bf16x2(a4, a5),
+             pack_bf16x2(a6, a7)};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Byte permute of the dword pair {hi_src, lo_src} (v_perm_b32): selector bytes
+// 0-3 pick bytes of lo_src, 4-7 bytes of hi_src.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+// Low 16-bit halves of a and b -> (b.lo << 16) | a.lo.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
+  return perm_b32(b, a, 0x05040100u);
+}
+// High 16-bit halves of a and b -> (b.hi << 16) | a.hi.
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return perm_b32(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ u32x4 ld_global_16B(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 zero_u32x4() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+}  // namespace fa

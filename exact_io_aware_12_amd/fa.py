@@ -1,0 +1,168 @@
+"""Thin ctypes binding of libfa355.so (fused exact attention for gfx950).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and torch's current HIP stream are passed to
+the C ABI, and every step of the computation runs in the library's kernels.
+PyTorch only supplies device memory and the stream. There is no fallback: if
+the library cannot be loaded, every call raises.
+
+The functions ``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes`` and
+``fa_strerror`` are the raw C entry points (ctypes). ``fwd`` / ``bwd`` are
+tensor-level wrappers with the same semantics.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_SCALE, FA_ERR_ALIGN, \
+    FA_ERR_WORKSPACE, FA_ERR_HIP = range(8)
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: error {code}: {strerror(code)}")
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m exact_io_aware_12_amd.build` "
+            "(there is no CPU fallback)")
+    # torch first, so the library binds to the HIP runtime torch already
+    # mapped (both carry the soname libamdhip64.so.7) and streams/pointers are
+    # shared.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises if it is missing)."""
+    return _load()
+
+
+# ----------------------------------------------------------------- raw C ABI
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
+    return _load().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, int(causal), stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+           scale, causal, stream) -> int:
+    return _load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+                          B, H, N, d, scale, int(causal), stream)
+
+
+def fa_bwd_workspace_bytes(B, H, N, d) -> int:
+    return _load().fa_bwd_workspace_bytes(B, H, N, d)
+
+
+def fa_strerror(code: int) -> str:
+    return _load().fa_strerror(code).decode()
+
+
+def strerror(code: int) -> str:
+    try:
+        return fa_strerror(code)
+    except ImportError:
+        return "library not loaded"
+
+
+# ----------------------------------------------------------------- tensors
+def _check(t, name, shape=None, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream_ptr(device, stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
+        stream=None):
+    """O, LSE = attention(q, k, v): bf16 [B,H,N,d] in, bf16 O and fp32 LSE out."""
+    import torch
+    _check(q, "q", dtype=torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    _check(k, "k", q.shape, torch.bfloat16)
+    _check(v, "v", q.shape, torch.bfloat16)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    _check(out, "out", q.shape, torch.bfloat16)
+    _check(lse, "lse", (B, H, N), torch.float32)
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, N, d, float(scale), causal, _stream_ptr(q.device, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None,
+        workspace=None, dq=None, dk=None, dv=None, stream=None):
+    """dQ, dK, dV of sum(O * dO) for O = fwd(q, k, v)."""
+    import torch
+    _check(q, "q", dtype=torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, q.shape, torch.bfloat16)
+    _check(lse, "lse", (B, H, N), torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _check(workspace, "workspace")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, q.shape, torch.bfloat16)
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                B, H, N, d, float(scale), causal, _stream_ptr(q.device, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,110 @@
+/*
+ * fa355.h -- C ABI of the fused exact attention library for AMD Instinct
+ * MI355X (gfx950): libfa355.so.
+ *
+ * The operation is exact softmax attention per (batch, head):
+ *     S = scale * Q K^T            (N x N, never written to memory)
+ *     P = softmax(S) row by row    (N x N, never written to memory)
+ *     O = P V
+ * as defined in "FlashAttention core principles" (lesson 1), section 1, and
+ * "FlashAttention and Triton" (chapter 19), section 19.1. The forward pass
+ * streams K/V tiles and keeps a running row max and row sum (lesson 1,
+ * sections 3-4; chapter 19, section 19.5); it saves one logsumexp per row.
+ * The backward pass recomputes S and P tile by tile from that statistic
+ * (lesson 1, section 5; the interview answer's "3. Recomputation" block).
+ *
+ * Common conventions
+ *   - Tensors Q, K, V, O, dO, dQ, dK, dV are bf16 (IEEE-754 binary32 with the
+ *     low 16 bits dropped, round-to-nearest-even), laid out [B, H, N, d]
+ *     contiguous (d fastest), in device memory of the current HIP device.
+ *   - LSE is fp32 [B, H, N]: the natural-log logsumexp of the row's scaled,
+ *     masked scores, i.e. m + ln(sum_j exp(s_j - m)).
+ *   - d (head dimension) must be 64 or 128. N >= 1 is any length (the last
+ *     tile may be partial). B, H >= 1. B*H*N*d must fit in 2^31 - 1 elements.
+ *   - scale multiplies Q K^T; any finite value, including 0, is accepted.
+ *   - causal != 0: query i attends key j iff j <= i (queries and keys share
+ *     the same positions 0..N-1).
+ *   - Every pointer must be 16-byte aligned. Outputs must not alias inputs.
+ *   - stream is a hipStream_t (NULL = the legacy default stream). Calls only
+ *     enqueue work and return; results are visible after the stream is
+ *     synchronised. Kernel faults surface at that synchronisation.
+ *   - Ownership: the caller allocates and frees every buffer, including the
+ *     backward workspace. The library keeps no state between calls, allocates
+ *     no memory and is safe to call from several host threads.
+ *   - Errors: 0 (FA_OK) on success, else one of the FA_ERR_* codes below.
+ *     Arguments are validated before any HIP call, so an invalid call launches
+ *     nothing and touches no memory. No C++ exception crosses this ABI.
+ */
+#ifndef FA355_H_
+#define FA355_H_
+
+#include <stddef.h>
+
+#if defined(__GNUC__)
+#define FA355_API __attribute__((visibility("default")))
+#else
+#define FA355_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or B*H*N*d overflows               */
+  FA_ERR_HEADDIM = 3,   /* d is not 64 or 128                                */
+  FA_ERR_SCALE = 4,     /* scale is NaN or infinite                          */
+  FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                  */
+  FA_ERR_WORKSPACE = 6, /* backward workspace NULL or smaller than required  */
+  FA_ERR_HIP = 7        /* the HIP runtime reported a launch error           */
+};
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [causal mask]) V and the per-row
+ * LSE (lesson 1, section 4 pseudocode and section 5's saved statistics).
+ *   q, k, v : in,  bf16 [B,H,N,d]
+ *   o       : out, bf16 [B,H,N,d]
+ *   lse     : out, fp32 [B,H,N]
+ */
+FA355_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * Size in bytes of the workspace fa_bwd needs for this shape: an fp32
+ * [B,H,N,d] dQ accumulator plus an fp32 [B,H,N] row statistic
+ * D_i = sum_c dO_ic O_ic (rounded up to 256 bytes each). Returns 0 when the
+ * shape is invalid.
+ */
+FA355_API size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass of fa_fwd (lesson 1, section 5): recomputes S and P per tile
+ * from Q, K and the saved LSE, and returns the gradients of sum(O * dO):
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D) * scale with
+ *   D_i = sum_j P_ij dP_ij = dO_i . O_i (the row sum over the whole row),
+ *   dQ = dS K,  dK = dS^T Q.
+ *   q, k, v, o, dout : in, bf16 [B,H,N,d]  (o and lse as returned by fa_fwd
+ *                      for the same q, k, v, scale and causal)
+ *   lse              : in, fp32 [B,H,N]
+ *   dq, dk, dv       : out, bf16 [B,H,N,d]
+ *   workspace        : scratch device memory of workspace_bytes bytes, at
+ *                      least fa_bwd_workspace_bytes(B,H,N,d); its contents on
+ *                      entry are ignored and on return are unspecified.
+ * dQ is accumulated in fp32 with atomic adds, so it may differ between runs
+ * in the last bits; dK and dV are deterministic.
+ */
+FA355_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+           float scale, int causal, void* stream);
+
+/* A static, human-readable description of an FA_* code. */
+FA355_API const char* fa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H_ */

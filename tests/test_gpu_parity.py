@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded bf16 inputs, element by element.
+
+Tolerances (max abs): O 2e-2, LSE 1e-3, dQ/dK/dV 5e-2.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_io_aware_12_amd import inputs as fi
+from parity_util import (TOL_GRAD, TOL_LSE, TOL_O, assert_close, bits_to_f64, from_gpu,
+                         to_gpu_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_io_aware_12_amd import fa as mod
+    mod.library()
+    return mod
+
+
+def _run_fwd(fa, qb, kb, vb, scale, causal):
+    import torch
+    q, k, v = to_gpu_bf16(qb), to_gpu_bf16(kb), to_gpu_bf16(vb)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse, (q, k, v)
+
+
+def _check_fwd(fa, B, H, N, d, causal, seed, scale=None, kscale=1.0):
+    print(f"[fwd] B={B} H={H} N={N} d={d} causal={causal} seed={seed}", flush=True)
+    shape = (B, H, N, d)
+    qb = fi.random_bf16(shape, seed)
+    kb = fi.random_bf16(shape, seed + 1, kscale)
+    vb = fi.random_bf16(shape, seed + 2)
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    o, lse, _ = _run_fwd(fa, qb, kb, vb, scale, causal)
+    ro, rl = oracle.attention_fwd(bits_to_f64(qb), bits_to_f64(kb), bits_to_f64(vb), scale, causal)
+    assert_close("O", from_gpu(o), ro, TOL_O)
+    assert_close("LSE", from_gpu(lse), rl, TOL_LSE)
+
+
+# Sizes span several query / key tiles and ragged tails (forward tiles: 128
+# queries x 64 keys at d=128, 128 x 128 at d=64).
+SMALL = [(1, 1, 1), (1, 1, 4), (1, 2, 37), (2, 1, 128), (1, 3, 200), (1, 1, 257),
+         (2, 4, 511), (1, 8, 640), (1, 1, 1000)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", SMALL)
+def test_fwd_small(fa, B, H, N, d, causal):
+    _check_fwd(fa, B, H, N, d, causal, seed=1000 + N + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_peaked_rows(fa, causal):
+    # Keys scaled by 3: peaked softmax rows, frequent max changes.
+    _check_fwd(fa, 1, 2, 777, 128, causal, seed=77, kscale=3.0)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.5])
+def test_fwd_other_scales(fa, scale):
+    _check_fwd(fa, 1, 2, 300, 64, True, seed=5, scale=scale)
+    _check_fwd(fa, 1, 2, 300, 128, False, seed=6, scale=scale)
+
+
+# ---------------------------------------------------------------- pins on the GPU
+def test_worked_example_on_gpu(fa):
+    n, d = 4, 64
+    q = np.zeros((1, 1, n, d), np.float32); q[0, 0, :, 0] = [1, 2, 3, 4]
+    k = np.zeros((1, 1, n, d), np.float32); k[0, 0, :, 0] = [1, 2, 3, 4]
+    v = np.zeros((1, 1, n, d), np.float32)
+    for j in range(n):
+        v[0, 0, j, j] = 1
+    o, lse, _ = _run_fwd(fa, fi.f32_to_bf16_bits(q), fi.f32_to_bf16_bits(k),
+                         fi.f32_to_bf16_bits(v), 1.0, False)
+    e = math.exp
+    tot = 1 + e(-1) + e(-2) + e(-3)
+    p = np.array([e(-3), e(-2), e(-1), 1]) / tot
+    assert abs(from_gpu(lse)[0, 0, 0] - (4 + math.log(tot))) <= TOL_LSE
+    assert np.abs(from_gpu(o)[0, 0, 0, :4] - p).max() <= TOL_O
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_scale_zero_closed_form_on_gpu(fa, d, causal):
+    N = 333
+    vb = fi.random_bf16((1, 2, N, d), 9)
+    qb, kb = fi.random_bf16((1, 2, N, d), 10), fi.random_bf16((1, 2, N, d), 11)
+    o, lse, _ = _run_fwd(fa, qb, kb, vb, 0.0, causal)
+    v = bits_to_f64(vb)
+    if causal:
+        ref = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+        rl = np.broadcast_to(np.log(np.arange(1, N + 1)), (1, 2, N))
+    else:
+        ref = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+        rl = np.full((1, 2, N), math.log(N))
+    assert_close("O", from_gpu(o), ref, TOL_O)
+    assert_close("LSE", from_gpu(lse), rl, TOL_LSE)
+
+
+def test_constant_v_and_identical_keys_on_gpu(fa):
+    N, d = 300, 128
+    qb = fi.random_bf16((1, 1, N, d), 12)
+    kb = np.tile(fi.random_bf16((1, 1, 1, d), 13), (1, 1, N, 1))
+    vrow = fi.random_bf16((1, 1, 1, d), 14)
+    o, _, _ = _run_fwd(fa, qb, kb, np.tile(vrow, (1, 1, N, 1)), 1 / math.sqrt(d), True)
+    assert_close("O const V", from_gpu(o), np.broadcast_to(bits_to_f64(vrow), (1, 1, N, d)), TOL_O)
+    vb = fi.random_bf16((1, 1, N, d), 15)
+    o, _, _ = _run_fwd(fa, qb, kb, vb, 1 / math.sqrt(d), True)
+    v = bits_to_f64(vb)
+    ref = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    assert_close("O same K", from_gpu(o), ref, TOL_O)
+
+
+def test_causal_row_zero_on_gpu(fa):
+    N, d = 130, 64
+    qb, kb, vb = (fi.random_bf16((2, 1, N, d), 20 + i) for i in range(3))
+    o, lse, _ = _run_fwd(fa, qb, kb, vb, 0.3, True)
+    q, k, v = bits_to_f64(qb), bits_to_f64(kb), bits_to_f64(vb)
+    assert np.abs(from_gpu(o)[:, 0, 0] - v[:, 0, 0]).max() <= 8e-3   # one bf16 rounding
+    ref = 0.3 * (q[:, 0, 0] * k[:, 0, 0]).sum(-1)
+    assert np.abs(from_gpu(lse)[:, 0, 0] - ref).max() <= TOL_LSE
+
+
+def test_fwd_deterministic_and_stream(fa):
+    import torch
+    shape = (1, 8, 1000, 128)
+    q, k, v = (to_gpu_bf16(fi.random_bf16(shape, 30 + i)) for i in range(3))
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = fa.fwd(q, k, v, causal=True)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------- backward
+def _check_bwd(fa, B, H, N, d, causal, seed, scale=None):
+    import torch
+    print(f"[bwd] B={B} H={H} N={N} d={d} causal={causal} seed={seed}", flush=True)
+    shape = (B, H, N, d)
+    qb, kb, vb, dob = (fi.random_bf16(shape, seed + i) for i in range(4))
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    o, lse, (q, k, v) = _run_fwd(fa, qb, kb, vb, scale, causal)
+    do = to_gpu_bf16(dob)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(bits_to_f64(qb), bits_to_f64(kb), bits_to_f64(vb),
+                                      bits_to_f64(dob), scale, causal)
+    assert_close("dQ", from_gpu(dq), rq, TOL_GRAD)
+    assert_close("dK", from_gpu(dk), rk, TOL_GRAD)
+    assert_close("dV", from_gpu(dv), rv, TOL_GRAD)
+
+
+BWD_SMALL = [(1, 1, 1), (1, 1, 5), (1, 2, 64), (2, 1, 129), (1, 3, 300), (1, 8, 512),
+             (1, 1, 1000)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", BWD_SMALL)
+def test_bwd_small(fa, B, H, N, d, causal):
+    _check_bwd(fa, B, H, N, d, causal, seed=2000 + N + d)
+
+
+def test_bwd_scale_zero_and_negative(fa):
+    _check_bwd(fa, 1, 2, 200, 128, True, seed=3, scale=0.0)
+    _check_bwd(fa, 1, 2, 200, 64, False, seed=4, scale=-0.3)
+
+
+# ---------------------------------------------------------------- the five workloads
+def _workload_fwd(fa, idx, heads=None):
+    import torch
+    inp = fi.make_inputs(idx)
+    w = inp.workload
+    print(f"[workload {idx}] {w.name}", flush=True)
+    q, k, v = to_gpu_bf16(inp.q), to_gpu_bf16(inp.k), to_gpu_bf16(inp.v)
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o_np, l_np = from_gpu(o), from_gpu(lse)
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if heads is not None:
+        sel = [sel[i] for i in heads]
+    for b, h in sel:
+        ro, rl = oracle.attention_fwd(bits_to_f64(inp.q[b, h]), bits_to_f64(inp.k[b, h]),
+                                      bits_to_f64(inp.v[b, h]), w.scale, w.causal)
+        assert_close(f"O[{b},{h}]", o_np[b, h], ro, TOL_O)
+        assert_close(f"LSE[{b},{h}]", l_np[b, h], rl, TOL_LSE)
+    return inp, (q, k, v, o, lse)
+
+
+def test_workload1_fwd(fa):
+    _workload_fwd(fa, 1)
+
+
+def test_workload2_fwd(fa):
+    _workload_fwd(fa, 2)
+
+
+def test_workload3_fwd_sampled_heads(fa):
+    # 64 heads; the oracle checks every row of 6 heads spread over both batches.
+    _workload_fwd(fa, 3, heads=[0, 13, 31, 32, 50, 63])
+
+
+def test_workload4_fwd_sampled_heads(fa):
+    # 16 heads of 16384 rows with K x 3; every row of the first and last head.
+    _workload_fwd(fa, 4, heads=[0, 15])
+
+
+def test_workload5_fwd_bwd(fa):
+    import torch
+    inp, (q, k, v, o, lse) = _workload_fwd(fa, 5, heads=[0, 17, 31])
+    w = inp.workload
+    do = to_gpu_bf16(inp.do)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    g = [from_gpu(t) for t in (dq, dk, dv)]
+    for b in range(w.B):
+        for h in range(w.H):
+            r = oracle.attention_bwd(bits_to_f64(inp.q[b, h]), bits_to_f64(inp.k[b, h]),
+                                     bits_to_f64(inp.v[b, h]), bits_to_f64(inp.do[b, h]),
+                                     w.scale, True)
+            for name, got, ref in zip(("dQ", "dK", "dV"), g, r):
+                assert_close(f"{name}[{b},{h}]", got[b, h], ref, TOL_GRAD)
