@@ -55,8 +55,60 @@ struct FwdCfg {
   static_assert(VLD * THREADS == (BN / 4) * KCH, "V tile split");
 };
 
+// Slack (log2 units) before the running max is moved; see the kernel.
+constexpr float kRescaleSlack = 8.f;
+
+// Max / min / sum over the NB*16 score registers of a lane (tree order, so
+// the compiler can use 3-input max and independent adds).
+template <int NB>
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[NB]) {
+  float r[NB * 4];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      r[kb * 4 + g] = fmaxf(fmaxf(s[kb][4 * g], s[kb][4 * g + 1]),
+                            fmaxf(s[kb][4 * g + 2], s[kb][4 * g + 3]));
+#pragma unroll
+  for (int w = NB * 4; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) r[i] = fmaxf(r[i], r[i + w / 2]);
+  return r[0];
+}
+template <int NB>
+__device__ __forceinline__ float tile_min(const f32x16 (&s)[NB]) {
+  float r[NB * 4];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      r[kb * 4 + g] = fminf(fminf(s[kb][4 * g], s[kb][4 * g + 1]),
+                            fminf(s[kb][4 * g + 2], s[kb][4 * g + 3]));
+#pragma unroll
+  for (int w = NB * 4; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) r[i] = fminf(r[i], r[i + w / 2]);
+  return r[0];
+}
+template <int NB>
+__device__ __forceinline__ float tile_sum(const f32x16 (&s)[NB]) {
+  float r[NB * 4];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      r[kb * 4 + g] = (s[kb][4 * g] + s[kb][4 * g + 1]) + (s[kb][4 * g + 2] + s[kb][4 * g + 3]);
+#pragma unroll
+  for (int w = NB * 4; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) r[i] = r[i] + r[i + w / 2];
+  return r[0];
+}
+
+// Two workgroups (8 waves) per CU: one wave's softmax runs while the other
+// wave on the same SIMD issues MFMAs, which a single wave cannot overlap.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fa_fwd_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     float* __restrict__ LSE, int BH, int N, int ntq, float c2, int xcd_group) {
@@ -119,7 +171,7 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < C::VLD; ++i) {
       const int u = tid + i * C::THREADS;
-      const int cc = u % C::KCH, g = u / C::KCH;
+      const int g = u % (C::BN / 4), cc = u / (C::BN / 4);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int key = kb0 + 4 * g + b;
@@ -139,8 +191,11 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
     }
 #pragma unroll
     for (int i = 0; i < C::VLD; ++i) {
+      // Consecutive lanes take consecutive 4-key groups of one 8-column
+      // chunk, so each transposed store instruction writes whole V^T rows
+      // (no LDS bank conflicts).
       const int u = tid + i * C::THREADS;
-      const int cc = u % C::KCH, g = u / C::KCH;
+      const int g = u % (C::BN / 4), cc = u / (C::BN / 4);
       // Keys 4g..4g+3: g = 4t + 2a + h lands at positions 16t + 8h + 4a + 0..3.
       const int pos = 16 * (g >> 2) + 8 * (g & 1) + 4 * ((g >> 1) & 1);
 #pragma unroll
@@ -191,75 +246,56 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
         }
       }
       // ---- online softmax statistics (base 2).
+      // The running max is only moved when a row's tile max exceeds it by
+      // more than kRescaleSlack (log2 units); otherwise the stale max is
+      // kept, so exp2(s - m) <= 2^kRescaleSlack and the rescale of O and l
+      // (64 multiplies per lane) is skipped. The result is unchanged: l and
+      // O are both taken relative to the same m, and LSE = m + log2(l).
       const bool need_mask = (CAUSAL && kbase + C::BN - 1 > qw) || (kbase + C::BN > N);
-      float m_new;
+      float tmax;
       if (need_mask) {
-        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
             const bool ok = key < N && (!CAUSAL || key <= qrow);
-            const float s = ok ? sacc[kb][i] * c2 : -INFINITY;
-            sacc[kb][i] = s;
-            mx = fmaxf(mx, s);
+            sacc[kb][i] = ok ? sacc[kb][i] * c2 : -INFINITY;
           }
-        mx = fmaxf(mx, swap_halves(mx));
-        m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-#pragma unroll
-        for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(sacc[kb][i] - m_use);
-        const float alpha = fast_exp2(m_run - m_use);
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) rs += sacc[kb][i];
-        l_run = l_run * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        tmax = tile_max<C::NB>(sacc);
+      } else if (c2 >= 0.f) {
+        tmax = tile_max<C::NB>(sacc) * c2;
       } else {
-        // No masked entry: reduce the raw dot products, then scale.
-        float mx;
-        if (c2 >= 0.f) {
-          mx = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        } else {
-          mx = INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fminf(mx, sacc[kb][i]);
-        }
-        mx *= c2;
-        mx = fmaxf(mx, swap_halves(mx));
-        m_new = fmaxf(m_run, mx);
-        const float nm = -m_new;
-#pragma unroll
-        for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(fmaf(sacc[kb][i], c2, nm));
-        const float alpha = fast_exp2(m_run - m_new);
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) rs += sacc[kb][i];
-        l_run = l_run * alpha + rs;
+        tmax = tile_min<C::NB>(sacc) * c2;
+      }
+      tmax = fmaxf(tmax, swap_halves(tmax));
+      const bool grow = tmax > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? tmax : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       }
-      m_run = m_new;
+      // Rows with no admissible key so far keep m = -inf; their scores are
+      // all -inf, so subtracting 0 gives p = 0.
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(sacc[kb][i] - m_use);
+      } else {
+        const float nm = -m_use;
+#pragma unroll
+        for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(fmaf(sacc[kb][i], c2, nm));
+      }
+      l_run += tile_sum<C::NB>(sacc);
       // ---- O^T += V^T P^T: 16 keys per MFMA; P^T straight from the
       // accumulator registers (k-slot s of half h = key 8*(s/4) + 4h + s%4).
 #pragma unroll
