@@ -41,6 +41,11 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// NaN-propagating max / min (v_maximum3_f32 / v_minimum3_f32 on gfx950; no
+// operand canonicalisation as fmaxf needs in IEEE mode).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+
 // 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // log2(x) (v_log_f32).

@@ -6,60 +6,81 @@
 // sum l, rescales the partial output by exp(m_old - m_new) when the max grows,
 // and normalises once at the end. The single-exponential update of the
 // interview answer ("2. Online Softmax") and of "FlashAttention and Triton",
-// section 19.12 is used: p = exp(s - m_new), l = alpha*l + rowsum(p).
+// section 19.12 is used: p = exp(s - m), l = alpha*l + rowsum(p).
 //
 // gfx950 mapping
-//   * Workgroup = 4 wave64s = BM = 128 query rows; each wave owns 32 rows.
+//   * Workgroup = 4 wave64s = BM = 128 query rows (32 per wave); two
+//     workgroups per CU (8 waves), so two waves share each SIMD.
 //   * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMAs:
-//     the accumulator puts one query per lane (column) and 16 keys per lane
-//     (rows), so the row max / row sum are in-lane reductions plus a single
-//     exchange between the two 32-lane halves.
-//   * O^T = V^T P^T, again one query per lane: P^T goes from the score
-//     accumulator into the B operand by register conversion only (bf16), and
-//     the per-row rescale alpha is a per-lane scalar.
+//     the accumulator holds one query per lane (column) and 16 keys per lane,
+//     so row max / row sum are in-lane reductions plus one exchange between
+//     the two 32-lane halves. O^T = V^T P^T keeps one query per lane as well:
+//     P^T goes from the score accumulator into the B operand by register
+//     conversion only, and the per-row rescale is a per-lane scalar.
 //   * Q stays in registers for the whole key loop (B operand of S^T).
-//   * K tiles sit row-major in LDS (A operand of S^T, one 16-byte read per
-//     lane per MFMA). V tiles are transposed while being written to LDS, with
-//     keys permuted inside each group of 16 to match the accumulator's row
-//     order, so each V^T operand is one 16-byte LDS read as well.
-//   * Register-staged double buffering: the global loads of tile j+1 are in
-//     flight while tile j is computed from LDS; one barrier per tile.
-//   * Softmax runs in the base-2 domain: scores are multiplied by
-//     scale*log2(e) in fp32 (Q is never pre-scaled in bf16) and exponentials
-//     use v_exp_f32. LSE is converted back to natural log on store.
+//   * K and V tiles go from HBM/L2 straight into LDS (global_load_lds_dwordx4,
+//     no staging registers), row-major with XOR-swizzled 16-byte chunks so the
+//     MFMA operand reads are free of bank conflicts. K operands are one
+//     ds_read_b128 per lane; V^T operands come from the row-major V tile
+//     through the transposing read ds_read_b64_tr_b16.
+//   * K is prefetched two tiles ahead and V one tile ahead (two LDS buffers
+//     each, one barrier per tile), and each wave is software-pipelined: the
+//     S^T MFMAs of tile j+1 are issued next to the softmax VALU work of tile j
+//     (one wave cannot overlap MFMA and VALU work unless its own instruction
+//     stream interleaves them).
+//   * Softmax runs in the base-2 domain with scale*log2(e) applied in fp32 (Q
+//     is never pre-scaled in bf16); the running max moves only when a tile
+//     max exceeds it by 2^8, which skips the O rescale on almost every tile
+//     without changing the result (l and O share the reference max). LSE is
+//     converted back to natural log on store.
 //   * Causal: tiles above the diagonal are never loaded or computed; only
-//     tiles that cross the diagonal (or the ragged end) evaluate the mask.
-//     Query tiles are issued heaviest first, and workgroups of one head are
-//     kept on one XCD (consecutive workgroup ids go to different XCDs).
+//     tiles crossing the diagonal (or the ragged end) evaluate the mask.
+//     Query tiles are issued heaviest first, and the workgroups of one head
+//     stay on one XCD (consecutive workgroup ids go to different XCDs).
+#include <type_traits>
+
 #include "fa_common.h"
 
 namespace fa {
 
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 128;              // query rows per workgroup
-  static constexpr int WAVES = 4;
-  static constexpr int THREADS = WAVES * 64;
-  static constexpr int BN = 8192 / D;         // keys per tile (16 KiB of K)
-  static constexpr int KS = D + 8;            // LDS row stride of K (bf16)
-  static constexpr int VS = BN + 8;           // LDS row stride of V^T (bf16)
-  static constexpr int KBUF = BN * KS;        // elements per K buffer
-  static constexpr int VBUF = D * VS;         // elements per V^T buffer
-  static constexpr int KCH = D / 8;           // 16-byte chunks per row
-  static constexpr int KLD = BN * KCH / THREADS;        // K chunks per thread
-  static constexpr int VLD = (BN / 4) * KCH / THREADS;  // V 4-row units per thread
-  static constexpr int NB = BN / 32;          // 32-key score blocks per tile
-  static constexpr int DB = D / 32;           // 32-wide output blocks
-  static constexpr int LDS_BYTES = 2 * (KBUF + VBUF) * 2;
-  static_assert(KLD * THREADS == BN * KCH, "K tile split");
-  static_assert(VLD * THREADS == (BN / 4) * KCH, "V tile split");
+  static constexpr int BM = 128;               // query rows per workgroup
+  static constexpr int THREADS = 256;          // 4 waves
+  static constexpr int BN = 64;                // keys per tile
+  static constexpr int RB = D * 2;             // bytes per K/V row in LDS
+  static constexpr int TILE_BYTES = BN * RB;   // 16 KiB (d=128) or 8 KiB (d=64)
+  static constexpr int LOADS = TILE_BYTES / 1024 / 4;   // 1 KiB DMAs per wave
+  static constexpr int ROWS_PER_LOAD = 1024 / RB;
+  static constexpr int NB = BN / 32;           // 32-key score blocks per tile
+  static constexpr int DB = D / 32;            // 32-wide output blocks
+  static constexpr int KS = D / 16;            // k-steps of S^T
 };
 
-// Slack (log2 units) before the running max is moved; see the kernel.
+// Byte offset of (row, 16-byte chunk c) of a K tile in LDS. The XOR makes the
+// 16 rows read by one MFMA operand load land in 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_off(int row, int c) {
+  if constexpr (D == 128) return row * 256 + ((c ^ (row & 15)) << 4);
+  else return row * 128 + ((c ^ ((row >> 1) & 7)) << 4);
+}
+// Byte offset of (row, column col) of a V tile in LDS: 64-byte blocks are
+// XOR-swizzled so the 4 rows of one transposing read hit distinct banks.
+template <int D>
+__device__ __forceinline__ int v_off(int row, int col) {
+  const int blk = col >> 5, in = (col & 31) * 2;
+  if constexpr (D == 128) return row * 256 + ((blk ^ (row & 3)) << 6) + in;
+  else return row * 128 + ((blk ^ ((row >> 1) & 1)) << 6) + in;
+}
+
+// Slack (log2 units) before the running max is moved.
 constexpr float kRescaleSlack = 8.f;
 
-// Max / min / sum over the NB*16 score registers of a lane (tree order, so
-// the compiler can use 3-input max and independent adds).
 template <int NB>
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB]) {
   float r[NB * 4];
@@ -67,12 +88,11 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB]) {
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      r[kb * 4 + g] = fmaxf(fmaxf(s[kb][4 * g], s[kb][4 * g + 1]),
-                            fmaxf(s[kb][4 * g + 2], s[kb][4 * g + 3]));
+      r[kb * 4 + g] = vmax(vmax(s[kb][4 * g], s[kb][4 * g + 1]), vmax(s[kb][4 * g + 2], s[kb][4 * g + 3]));
 #pragma unroll
   for (int w = NB * 4; w > 1; w >>= 1)
 #pragma unroll
-    for (int i = 0; i < w / 2; ++i) r[i] = fmaxf(r[i], r[i + w / 2]);
+    for (int i = 0; i < w / 2; ++i) r[i] = vmax(r[i], r[i + w / 2]);
   return r[0];
 }
 template <int NB>
@@ -82,12 +102,11 @@ __device__ __forceinline__ float tile_min(const f32x16 (&s)[NB]) {
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      r[kb * 4 + g] = fminf(fminf(s[kb][4 * g], s[kb][4 * g + 1]),
-                            fminf(s[kb][4 * g + 2], s[kb][4 * g + 3]));
+      r[kb * 4 + g] = vmin(vmin(s[kb][4 * g], s[kb][4 * g + 1]), vmin(s[kb][4 * g + 2], s[kb][4 * g + 3]));
 #pragma unroll
   for (int w = NB * 4; w > 1; w >>= 1)
 #pragma unroll
-    for (int i = 0; i < w / 2; ++i) r[i] = fminf(r[i], r[i + w / 2]);
+    for (int i = 0; i < w / 2; ++i) r[i] = vmin(r[i], r[i + w / 2]);
   return r[0];
 }
 template <int NB>
@@ -105,20 +124,62 @@ __device__ __forceinline__ float tile_sum(const f32x16 (&s)[NB]) {
   return r[0];
 }
 
-// Two workgroups (8 waves) per CU: one wave's softmax runs while the other
-// wave on the same SIMD issues MFMAs, which a single wave cannot overlap.
+// Issue this wave's share of the DMA of one K or V tile (rows kb0..kb0+BN-1;
+// rows past N read row N-1) into an LDS buffer: LOADS x 1 KiB per wave. Lane
+// i of a load writes LDS bytes [16i, 16i+16) of its 1 KiB, so each lane
+// fetches the global chunk that the swizzle places there.
+template <int D, bool IS_V>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint8_t* lds,
+                                         int kb0, int N, int w, int lane) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int lrow = (w * C::LOADS + i) * C::ROWS_PER_LOAD;   // first row of this 1 KiB
+    const int row = lrow + lane / (C::RB / 16);
+    const int pc = lane % (C::RB / 16);                       // physical 16-byte chunk
+    int col;                                                  // logical first column
+    if constexpr (!IS_V) {
+      int c;
+      if constexpr (D == 128) c = pc ^ (row & 15);
+      else c = pc ^ ((row >> 1) & 7);
+      col = c * 8;
+    } else {
+      const int pb = pc >> 2;
+      int lb;
+      if constexpr (D == 128) lb = pb ^ (row & 3);
+      else lb = pb ^ ((row >> 1) & 1);
+      col = lb * 32 + (pc & 3) * 8;
+    }
+    const int key = min(kb0 + row, N - 1);
+    const uint16_t* g = src + (size_t)key * D + col;
+    __builtin_amdgcn_global_load_lds((const GLB_AS void*)g,
+                                     (LDS_AS void*)(lds + lrow * C::RB), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_dma() {
+  // s_waitcnt vmcnt(0): this wave's outstanding global->LDS copies are done.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     float* __restrict__ LSE, int BH, int N, int ntq, float c2, int xcd_group) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (C::KBUF + C::VBUF)];
-  uint16_t* Ks = smem;                      // [2][BN][KS]
-  uint16_t* Vt = smem + 2 * C::KBUF;        // [2][D][VS]
+  // Four distinct LDS objects (not one indexed array): the loop below is
+  // unrolled by two so each access names its buffer statically, which lets
+  // the compiler see that an in-flight DMA into one buffer does not alias
+  // the reads of another (otherwise it waits for the DMA before every read).
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[C::TILE_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Workgroup -> (head, query tile).
@@ -141,116 +202,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int qw = q0 + w * 32;          // first query row of this wave
   const int qrow = qw + l32;           // this lane's query row
   const size_t off = (size_t)head * N * D;
-  const uint16_t* Qh = Q + off;
   const uint16_t* Kh = K + off;
   const uint16_t* Vh = V + off;
 
-  // Q rows of this lane as B operands (k-slots = head-dim positions).
-  bf16x8 qreg[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 t = qrow < N ? ld_global_16B(Qh + (size_t)qrow * D + ks * 16 + hi * 8) : zero_u32x4();
-    qreg[ks] = __builtin_bit_cast(bf16x8, t);
-  }
-
   const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
   const int nt = (kend + C::BN - 1) / C::BN;
+  // Tiles this wave computes: 0 .. ntw-1 (causal waves stop at the diagonal).
+  const int ntw = CAUSAL ? min(nt, (min(N, qw + 32) + C::BN - 1) / C::BN) : nt;
 
-  u32x4 kreg[C::KLD];
-  u32x4 vreg[C::VLD][4];
+  // Prologue DMA: K0, V0, K1.
+  dma_tile<D, false>(Kh, k_lds0, 0, N, w, lane);
+  dma_tile<D, true>(Vh, v_lds0, 0, N, w, lane);
+  if (nt > 1) dma_tile<D, false>(Kh, k_lds1, C::BN, N, w, lane);
 
-  auto load_tile = [&](int j) {
-    const int kb0 = j * C::BN;
+  // Q rows of this lane as B operands (rows past N read row N-1; never stored).
+  bf16x8 qreg[C::KS];
+  {
+    const uint16_t* qp = Q + off + (size_t)min(qrow, N - 1) * D + hi * 8;
 #pragma unroll
-    for (int i = 0; i < C::KLD; ++i) {
-      const int u = tid + i * C::THREADS;
-      const int r = u / C::KCH, cc = u % C::KCH;
-      const int key = kb0 + r;
-      kreg[i] = key < N ? ld_global_16B(Kh + (size_t)key * D + cc * 8) : zero_u32x4();
-    }
-#pragma unroll
-    for (int i = 0; i < C::VLD; ++i) {
-      const int u = tid + i * C::THREADS;
-      const int g = u % (C::BN / 4), cc = u / (C::BN / 4);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int key = kb0 + 4 * g + b;
-        vreg[i][b] = key < N ? ld_global_16B(Vh + (size_t)key * D + cc * 8) : zero_u32x4();
-      }
-    }
-  };
+    for (int ks = 0; ks < C::KS; ++ks)
+      qreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(qp + ks * 16));
+  }
 
-  auto store_tile = [&](int buf) {
-    uint16_t* kd = Ks + buf * C::KBUF;
-    uint16_t* vd = Vt + buf * C::VBUF;
+  // Per-lane LDS read offsets.
+  int koff[C::NB][C::KS];
 #pragma unroll
-    for (int i = 0; i < C::KLD; ++i) {
-      const int u = tid + i * C::THREADS;
-      const int r = u / C::KCH, cc = u % C::KCH;
-      *reinterpret_cast<u32x4*>(kd + r * C::KS + cc * 8) = kreg[i];
-    }
+  for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
-    for (int i = 0; i < C::VLD; ++i) {
-      // Consecutive lanes take consecutive 4-key groups of one 8-column
-      // chunk, so each transposed store instruction writes whole V^T rows
-      // (no LDS bank conflicts).
-      const int u = tid + i * C::THREADS;
-      const int g = u % (C::BN / 4), cc = u / (C::BN / 4);
-      // Keys 4g..4g+3: g = 4t + 2a + h lands at positions 16t + 8h + 4a + 0..3.
-      const int pos = 16 * (g >> 2) + 8 * (g & 1) + 4 * ((g >> 1) & 1);
+    for (int ks = 0; ks < C::KS; ++ks) koff[kb][ks] = k_off<D>(kb * 32 + l32, 2 * ks + hi);
+  // Transposing reads: lane (group g = lane/16, source s = lane%16) points at
+  // V row 16t + 8*half + 4*hi + s/4, columns 32*db + 16*(g&1) + 4*(s&3) .. +3.
+  int voff[C::BN / 16][2][C::DB];
+  {
+    const int g = lane >> 4, s = lane & 15;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dw = e >> 1;
-        uint32_t w0, w1;
-        if (e & 1) {
-          w0 = pack_hi16(vreg[i][0][dw], vreg[i][1][dw]);
-          w1 = pack_hi16(vreg[i][2][dw], vreg[i][3][dw]);
-        } else {
-          w0 = pack_lo16(vreg[i][0][dw], vreg[i][1][dw]);
-          w1 = pack_lo16(vreg[i][2][dw], vreg[i][3][dw]);
-        }
-        u32x2 pr = {w0, w1};
-        *reinterpret_cast<u32x2*>(vd + (cc * 8 + e) * C::VS + pos) = pr;
-      }
-    }
-  };
+    for (int t = 0; t < C::BN / 16; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+          voff[t][h][db] = v_off<D>(16 * t + 8 * h + 4 * hi + (s >> 2), 32 * db + 16 * (g & 1) + 4 * (s & 3));
+  }
 
   f32x16 oacc[C::DB];
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) oacc[i] = zero16();
-  float m_run = -INFINITY;   // running max of this lane's row (log2 domain)
+  float m_run = -INFINITY;   // running (reference) max of this lane's row, log2 domain
   float l_run = 0.f;         // running sum over this lane's half of the keys
 
-  load_tile(0);
-  store_tile(0);
-
-  for (int j = 0; j < nt; ++j) {
-    __syncthreads();
-    if (j + 1 < nt) load_tile(j + 1);
-    const int buf = j & 1;
-    const int kbase = j * C::BN;
-    const bool active = !CAUSAL || kbase <= qw + 31;
-    if (active) {
-      const uint16_t* kd = Ks + buf * C::KBUF;
-      const uint16_t* vd = Vt + buf * C::VBUF;
-      // ---- S^T = K Q^T for this tile (NB blocks of 32 keys x 32 queries).
-      f32x16 sacc[C::NB];
+  auto scores = [&](f32x16 (&s)[C::NB], const uint8_t* kt) {
 #pragma unroll
-      for (int kb = 0; kb < C::NB; ++kb) {
-        sacc[kb] = zero16();
+    for (int kb = 0; kb < C::NB; ++kb) {
+      s[kb] = zero16();
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              kd + (kb * 32 + l32) * C::KS + ks * 16 + hi * 8);
-          sacc[kb] = mfma_32x32x16(a, qreg[ks], sacc[kb]);
-        }
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[kb][ks]);
+        s[kb] = mfma_32x32x16(a, qreg[ks], s[kb]);
       }
-      // ---- online softmax statistics (base 2).
-      // The running max is only moved when a row's tile max exceeds it by
-      // more than kRescaleSlack (log2 units); otherwise the stale max is
-      // kept, so exp2(s - m) <= 2^kRescaleSlack and the rescale of O and l
-      // (64 multiplies per lane) is skipped. The result is unchanged: l and
-      // O are both taken relative to the same m, and LSE = m + log2(l).
+    }
+  };
+
+  f32x16 scur[C::NB], snext[C::NB];
+  wait_dma();
+  __syncthreads();
+  if (ntw > 0) scores(scur, k_lds0);
+  __syncthreads();   // K buffer 0 is refilled by the first tile step
+
+  // One tile step; P is the parity of j (K_j and V_j live in buffer P).
+  auto step = [&](auto parity, int j) {
+    constexpr int P = decltype(parity)::value;
+    uint8_t* const k_this = P ? k_lds1 : k_lds0;   // K_j (done), refilled with K_{j+2}
+    uint8_t* const k_next = P ? k_lds0 : k_lds1;   // K_{j+1}
+    uint8_t* const v_this = P ? v_lds1 : v_lds0;   // V_j
+    uint8_t* const v_next = P ? v_lds0 : v_lds1;   // refilled with V_{j+1}
+    const int kbase = j * C::BN;
+    if (j + 2 < nt) dma_tile<D, false>(Kh, k_this, (j + 2) * C::BN, N, w, lane);
+    if (j + 1 < nt) dma_tile<D, true>(Vh, v_next, (j + 1) * C::BN, N, w, lane);
+    if (j < ntw) {
+      // ---- S^T of the next tile (MFMA) next to the softmax of this one (VALU).
+      if (j + 1 < ntw) scores(snext, k_next);
       const bool need_mask = (CAUSAL && kbase + C::BN - 1 > qw) || (kbase + C::BN > N);
       float tmax;
       if (need_mask) {
@@ -260,15 +290,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int i = 0; i < 16; ++i) {
             const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
             const bool ok = key < N && (!CAUSAL || key <= qrow);
-            sacc[kb][i] = ok ? sacc[kb][i] * c2 : -INFINITY;
+            scur[kb][i] = ok ? scur[kb][i] * c2 : -INFINITY;
           }
-        tmax = tile_max<C::NB>(sacc);
+        tmax = tile_max<C::NB>(scur);
       } else if (c2 >= 0.f) {
-        tmax = tile_max<C::NB>(sacc) * c2;
+        tmax = tile_max<C::NB>(scur) * c2;
       } else {
-        tmax = tile_min<C::NB>(sacc) * c2;
+        tmax = tile_min<C::NB>(scur) * c2;
       }
-      tmax = fmaxf(tmax, swap_halves(tmax));
+      tmax = vmax(tmax, swap_halves(tmax));
       const bool grow = tmax > m_run + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float m_new = grow ? tmax : m_run;
@@ -280,39 +310,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       }
-      // Rows with no admissible key so far keep m = -inf; their scores are
-      // all -inf, so subtracting 0 gives p = 0.
+      // A row with no admissible key so far keeps m = -inf (all its scores
+      // are -inf): subtract 0 so that p = 0.
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(sacc[kb][i] - m_use);
+          for (int i = 0; i < 16; ++i) scur[kb][i] = fast_exp2(scur[kb][i] - m_use);
       } else {
         const float nm = -m_use;
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[kb][i] = fast_exp2(fmaf(sacc[kb][i], c2, nm));
+          for (int i = 0; i < 16; ++i) scur[kb][i] = fast_exp2(fmaf(scur[kb][i], c2, nm));
       }
-      l_run += tile_sum<C::NB>(sacc);
-      // ---- O^T += V^T P^T: 16 keys per MFMA; P^T straight from the
-      // accumulator registers (k-slot s of half h = key 8*(s/4) + 4h + s%4).
+      l_run += tile_sum<C::NB>(scur);
+      // ---- O^T += V^T P^T: 16 keys per MFMA; k-slot s of half h is key
+      // 8*(s/4) + 4h + s%4 of the 16, both in P^T (accumulator rows) and in
+      // the V^T operand (two transposing reads of 4 keys each).
 #pragma unroll
       for (int t = 0; t < C::BN / 16; ++t) {
-        const f32x16& p = sacc[t >> 1];
+        const f32x16& p = scur[t >> 1];
         const int r0 = (t & 1) * 8;
         const bf16x8 pb = pack_bf16x8(p[r0 + 0], p[r0 + 1], p[r0 + 2], p[r0 + 3],
                                       p[r0 + 4], p[r0 + 5], p[r0 + 6], p[r0 + 7]);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              vd + (db * 32 + l32) * C::VS + 16 * t + 8 * hi);
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(v_this + voff[t][0][db]));
+          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(v_this + voff[t][1][db]));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[db] = mfma_32x32x16(a, pb, oacc[db]);
         }
       }
+#pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb) scur[kb] = snext[kb];
     }
-    if (j + 1 < nt) store_tile((j + 1) & 1);
+    wait_dma();
+    __syncthreads();
+  };
+
+  for (int j = 0; j < nt; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // ---- epilogue: O = O / l, LSE = ln2 * (m + log2 l).
