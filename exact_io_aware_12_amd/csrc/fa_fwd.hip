@@ -162,7 +162,11 @@ __device__ __forceinline__ void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int D, bool CAUSAL>
+// POS: scale > 0. Then a masked score can be stored as a raw -inf (its
+// scaled value is -inf as well) and every tile uses exp2(fma(s, c2, -m)).
+// Otherwise (scale <= 0, rare) every tile is scaled first and uses
+// exp2(s - m).
+template <int D, bool CAUSAL, bool POS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
@@ -224,24 +228,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       qreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(qp + ks * 16));
   }
 
-  // Per-lane LDS read offsets.
-  int koff[C::NB][C::KS];
+  // Per-lane LDS read offsets. K operand (row kb*32 + l32, chunk 2ks + hi):
+  // the row's swizzle only depends on l32, so the 32-row block kb is an
+  // immediate offset and one register per k-step holds the XORed chunk.
+  int koff[C::KS];
 #pragma unroll
-  for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) koff[kb][ks] = k_off<D>(kb * 32 + l32, 2 * ks + hi);
-  // Transposing reads: lane (group g = lane/16, source s = lane%16) points at
-  // V row 16t + 8*half + 4*hi + s/4, columns 32*db + 16*(g&1) + 4*(s&3) .. +3.
-  int voff[C::BN / 16][2][C::DB];
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = k_off<D>(l32, 2 * ks + hi);
+  // Transposing V reads: lane (group g = lane/16, source s = lane%16) points
+  // at V row 16t + 8*half + 4*hi + s/4, columns 32*db + 16*(g&1) + 4*(s&3)..+3.
+  // The swizzle of those rows only depends on s, so t and the half are
+  // immediate offsets and one register per 32-column block db remains.
+  int voff[C::DB];
   {
-    const int g = lane >> 4, s = lane & 15;
+    const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
-    for (int t = 0; t < C::BN / 16; ++t)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          voff[t][h][db] = v_off<D>(16 * t + 8 * h + 4 * hi + (s >> 2), 32 * db + 16 * (g & 1) + 4 * (s & 3));
+    for (int db = 0; db < C::DB; ++db)
+      voff[db] = v_off<D>(4 * hi + (sl >> 2), 32 * db + 16 * (g & 1) + 4 * (sl & 3));
   }
 
   f32x16 oacc[C::DB];
@@ -250,101 +252,149 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = -INFINITY;   // running (reference) max of this lane's row, log2 domain
   float l_run = 0.f;         // running sum over this lane's half of the keys
 
-  auto scores = [&](f32x16 (&s)[C::NB], const uint8_t* kt) {
+  auto scores = [&](f32x16 (&s)[C::NB], const uint8_t* kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < C::NB; ++kb) {
       s[kb] = zero16();
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[kb][ks]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * C::RB + koff[ks]);
         s[kb] = mfma_32x32x16(a, qreg[ks], s[kb]);
       }
     }
   };
 
-  f32x16 scur[C::NB], snext[C::NB];
+  f32x16 sacc[2][C::NB];   // scores of tiles j (parity of j) and j+1
+
+  // Statistics of a freshly computed score tile: mask it if it crosses the
+  // diagonal or the ragged end (masked tiles are left scaled by c2, others
+  // raw), take its max, exchange it between the two row halves, and move
+  // the reference max if it grew by more than kRescaleSlack (rare: O and l
+  // are rescaled then). Returns whether the tile was masked.
+  auto tile_stats = [&](f32x16 (&s)[C::NB], int kbase) __attribute__((always_inline)) {
+    const bool masked = (CAUSAL && kbase + C::BN - 1 > qw) || (kbase + C::BN > N);
+    if (masked) {
+#pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          const bool ok = key < N && (!CAUSAL || key <= qrow);
+          if constexpr (POS) s[kb][i] = ok ? s[kb][i] : -INFINITY;
+          else s[kb][i] = ok ? s[kb][i] * c2 : -INFINITY;
+        }
+    } else if constexpr (!POS) {
+#pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] *= c2;
+    }
+    float tmax = tile_max<C::NB>(s);
+    if constexpr (POS) tmax *= c2;
+    tmax = vmax(tmax, swap_halves(tmax));
+    const bool grow = tmax > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+  };
+
+  // The branch-free body of a tile step: S^T of the next tile (MFMA, when
+  // HAS_NEXT) beside p = exp2(s - m), the row sum, the bf16 packing and
+  // O^T += V^T P^T of this tile, so the scheduler can interleave MFMA and
+  // VALU work of one wave.
+  auto tile_body = [&](f32x16 (&scur)[C::NB], f32x16 (&snext)[C::NB], const uint8_t* k_next,
+                       const uint8_t* v_this) __attribute__((always_inline)) {
+    scores(snext, k_next);
+    // A row with no admissible key so far keeps m = -inf (all its scores
+    // are -inf): subtract 0 so that p = 0.
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    if constexpr (!POS) {
+#pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) scur[kb][i] = fast_exp2(scur[kb][i] - m_use);
+    } else {
+      const float nm = -m_use;
+#pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) scur[kb][i] = fast_exp2(fmaf(scur[kb][i], c2, nm));
+    }
+    l_run += tile_sum<C::NB>(scur);
+    // O^T += V^T P^T: 16 keys per MFMA; k-slot s of half h is key
+    // 8*(s/4) + 4h + s%4 of the 16, both in P^T (accumulator rows) and in
+    // the V^T operand (two transposing reads of 4 keys each).
+#pragma unroll
+    for (int t = 0; t < C::BN / 16; ++t) {
+      const f32x16& p = scur[t >> 1];
+      const int r0 = (t & 1) * 8;
+      const bf16x8 pb = pack_bf16x8(p[r0 + 0], p[r0 + 1], p[r0 + 2], p[r0 + 3],
+                                    p[r0 + 4], p[r0 + 5], p[r0 + 6], p[r0 + 7]);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const uint8_t* vp = v_this + 16 * t * C::RB + voff[db];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)vp);
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp + 8 * C::RB));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = mfma_32x32x16(a, pb, oacc[db]);
+      }
+    }
+    // Instruction order for this block (one wave issues in order, so MFMA
+    // work only overlaps VALU work that sits between the MFMAs): the S^T
+    // MFMAs of the next tile each carry one LDS operand read and the
+    // fma+exp of two scores; the O^T MFMAs each carry two V^T reads and
+    // the row-sum / bf16-pack work.
+    constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < C::NB * C::KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kValu, 4, 0);
+    }
+
+#pragma unroll
+    for (int i = 0; i < (C::BN / 16) * C::DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kValu, 3, 0);
+    }
+  };
+
   wait_dma();
   __syncthreads();
-  if (ntw > 0) scores(scur, k_lds0);
+  if (ntw > 0) {
+    scores(sacc[0], k_lds0);
+    tile_stats(sacc[0], 0);
+  }
   __syncthreads();   // K buffer 0 is refilled by the first tile step
 
   // One tile step; P is the parity of j (K_j and V_j live in buffer P).
-  auto step = [&](auto parity, int j) {
+  // Entering it, sacc[P] holds tile j's scores (masked, and with the
+  // reference max already updated for them).
+  auto step = [&](auto parity, int j) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
     uint8_t* const k_this = P ? k_lds1 : k_lds0;   // K_j (done), refilled with K_{j+2}
     uint8_t* const k_next = P ? k_lds0 : k_lds1;   // K_{j+1}
     uint8_t* const v_this = P ? v_lds1 : v_lds0;   // V_j
     uint8_t* const v_next = P ? v_lds0 : v_lds1;   // refilled with V_{j+1}
-    const int kbase = j * C::BN;
     if (j + 2 < nt) dma_tile<D, false>(Kh, k_this, (j + 2) * C::BN, N, w, lane);
     if (j + 1 < nt) dma_tile<D, true>(Vh, v_next, (j + 1) * C::BN, N, w, lane);
+    f32x16 (&scur)[C::NB] = sacc[P];
+    f32x16 (&snext)[C::NB] = sacc[P ^ 1];
     if (j < ntw) {
-      // ---- S^T of the next tile (MFMA) next to the softmax of this one (VALU).
-      if (j + 1 < ntw) scores(snext, k_next);
-      const bool need_mask = (CAUSAL && kbase + C::BN - 1 > qw) || (kbase + C::BN > N);
-      float tmax;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const bool ok = key < N && (!CAUSAL || key <= qrow);
-            scur[kb][i] = ok ? scur[kb][i] * c2 : -INFINITY;
-          }
-        tmax = tile_max<C::NB>(scur);
-      } else if (c2 >= 0.f) {
-        tmax = tile_max<C::NB>(scur) * c2;
-      } else {
-        tmax = tile_min<C::NB>(scur) * c2;
-      }
-      tmax = vmax(tmax, swap_halves(tmax));
-      const bool grow = tmax > m_run + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? tmax : m_run;
-        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-      // A row with no admissible key so far keeps m = -inf (all its scores
-      // are -inf): subtract 0 so that p = 0.
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) scur[kb][i] = fast_exp2(scur[kb][i] - m_use);
-      } else {
-        const float nm = -m_use;
-#pragma unroll
-        for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) scur[kb][i] = fast_exp2(fmaf(scur[kb][i], c2, nm));
-      }
-      l_run += tile_sum<C::NB>(scur);
-      // ---- O^T += V^T P^T: 16 keys per MFMA; k-slot s of half h is key
-      // 8*(s/4) + 4h + s%4 of the 16, both in P^T (accumulator rows) and in
-      // the V^T operand (two transposing reads of 4 keys each).
-#pragma unroll
-      for (int t = 0; t < C::BN / 16; ++t) {
-        const f32x16& p = scur[t >> 1];
-        const int r0 = (t & 1) * 8;
-        const bf16x8 pb = pack_bf16x8(p[r0 + 0], p[r0 + 1], p[r0 + 2], p[r0 + 3],
-                                      p[r0 + 4], p[r0 + 5], p[r0 + 6], p[r0 + 7]);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(v_this + voff[t][0][db]));
-          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(v_this + voff[t][1][db]));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = mfma_32x32x16(a, pb, oacc[db]);
-        }
-      }
-#pragma unroll
-      for (int kb = 0; kb < C::NB; ++kb) scur[kb] = snext[kb];
+      // The next tile's scores are computed even on this wave's last tile
+      // (then from whatever the other K buffer holds, and never used): one
+      // code path keeps the register allocation of the loop simple.
+      tile_body(scur, snext, k_next, v_this);
+      if (j + 1 < ntw) tile_stats(snext, (j + 1) * C::BN);
     }
     wait_dma();
     __syncthreads();
@@ -373,7 +423,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool POS>
 static hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              uint16_t* o, float* lse, int BH, int N, float scale,
                              hipStream_t stream) {
@@ -382,7 +432,7 @@ static hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_
   const int xcd_group = (BH % 8 == 0) ? BH / 8 : 0;
   const float c2 = scale * kLog2e;
   dim3 grid((unsigned)(ntq * BH)), block(C::THREADS);
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), grid, block, 0, stream,
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, POS>), grid, block, 0, stream,
                      q, k, v, o, lse, BH, N, ntq, c2, xcd_group);
   return hipGetLastError();
 }
@@ -390,11 +440,20 @@ static hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_
 hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* o, float* lse, int BH, int N, int d, float scale,
                         bool causal, hipStream_t stream) {
-  if (d == 128)
-    return causal ? launch_fwd<128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_fwd<128, false>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_fwd<64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_fwd<64, false>(q, k, v, o, lse, BH, N, scale, stream);
+  const bool pos = scale > 0.f;
+#define FA_FWD_CASE(DD, CC, PP) \
+  if (d == DD && causal == CC && pos == PP) \
+    return launch_fwd<DD, CC, PP>(q, k, v, o, lse, BH, N, scale, stream);
+  FA_FWD_CASE(128, true, true)
+  FA_FWD_CASE(128, false, true)
+  FA_FWD_CASE(64, true, true)
+  FA_FWD_CASE(64, false, true)
+  FA_FWD_CASE(128, true, false)
+  FA_FWD_CASE(128, false, false)
+  FA_FWD_CASE(64, true, false)
+  FA_FWD_CASE(64, false, false)
+#undef FA_FWD_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa
