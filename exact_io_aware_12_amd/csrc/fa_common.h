@@ -56,6 +56,20 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of x over lanes l and l ^ 32, via v_permlane32_swap (one VALU
+// exchange, no LDS round trip): swapping x with itself leaves x of the low
+// half in one result and x of the high half in the other, on every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Two fp32 -> two bf16 (round to nearest even), packed in one dword.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 f = {lo, hi};

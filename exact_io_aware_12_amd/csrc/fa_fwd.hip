@@ -254,14 +254,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   auto scores = [&](f32x16 (&s)[C::NB], const uint8_t* kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < C::NB; ++kb) {
-      s[kb] = zero16();
+    for (int kb = 0; kb < C::NB; ++kb) s[kb] = zero16();
+    // k-step outer: consecutive MFMAs alternate between the independent
+    // accumulators of the 32-key blocks instead of waiting on one chain.
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * C::RB + koff[ks]);
         s[kb] = mfma_32x32x16(a, qreg[ks], s[kb]);
       }
-    }
   };
 
   f32x16 sacc[2][C::NB];   // scores of tiles j (parity of j) and j+1
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     float tmax = tile_max<C::NB>(s);
     if constexpr (POS) tmax *= c2;
-    tmax = vmax(tmax, swap_halves(tmax));
+    tmax = halves_max(tmax);
     const bool grow = tmax > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? tmax : m_run;
@@ -347,23 +349,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     // Instruction order for this block (one wave issues in order, so MFMA
-    // work only overlaps VALU work that sits between the MFMAs): the S^T
-    // MFMAs of the next tile each carry one LDS operand read and the
-    // fma+exp of two scores; the O^T MFMAs each carry two V^T reads and
-    // the row-sum / bf16-pack work.
+    // work only overlaps VALU work that sits between the MFMAs, and LDS
+    // latency is only hidden by reads issued several MFMAs ahead): the S^T
+    // MFMAs of the next tile each carry two LDS reads (the remaining K
+    // operands, then the first V^T operands of the O^T phase) and the
+    // fma+exp of two scores; the O^T MFMAs each carry one V^T read and the
+    // row-sum / bf16-pack work.
     constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
     __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
 #pragma unroll
     for (int i = 0; i < C::NB * C::KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
       __builtin_amdgcn_sched_group_barrier(kValu, 4, 0);
     }
-
 #pragma unroll
     for (int i = 0; i < (C::BN / 16) * C::DB; ++i) {
       __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kValu, 3, 0);
     }
   };
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // ---- epilogue: O = O / l, LSE = ln2 * (m + log2 l).
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = halves_sum(l_run);
   if (qrow < N) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = O + off + (size_t)qrow * D;
