@@ -10,9 +10,9 @@
 //
 // Three kernels on the caller's stream:
 //   1. fa_bwd_pre:   D_i = dO_i . O_i (fp32) and zero the fp32 dQ accumulator.
-//   2. fa_bwd_main:  one workgroup per 128-key tile (4 wave64s x 32 keys); the
-//      loop runs over 64-query tiles (outer loop over K/V, inner over Q, so
-//      dK and dV stay in registers for the whole loop).
+//   2. fa_bwd_main:  one workgroup per 128-key tile (4 wave64s x 32 keys, one
+//      wave per SIMD); the loop runs over 64-query tiles (outer loop over K/V,
+//      inner over Q, so dK and dV stay in registers for the whole loop).
 //   3. fa_bwd_dq:    dQ = scale * accumulator, rounded to bf16.
 //
 // gfx950 mapping of the main kernel (32x32x16 bf16 MFMAs, fp32 accumulate):
@@ -20,13 +20,18 @@
 //     operands K and V of this wave's 32 keys live in registers), so P and dS
 //     sit in registers in exactly the layout the B operand of
 //     dV^T += dO^T P and dK^T += Q^T dS needs (k-slots are queries).
-//   * Q and dO tiles are stored in LDS twice: row-major (A operands of S and
-//     dP) and transposed with queries permuted inside groups of 16 to match
-//     the accumulator's row order (A operands of dV^T and dK^T).
-//   * dQ needs dS with one query per lane, so dS goes through LDS (bf16) and
-//     dQ += dS K is accumulated in fp32 with hardware float atomics.
-//   * The next Q/dO tile is prefetched into registers during the compute;
-//     two barriers per tile.
+//   * Q and dO tiles go from HBM/L2 straight into LDS (global_load_lds_dwordx4,
+//     double-buffered) in one XOR swizzle that serves both the row-major
+//     operand reads of S and dP (ds_read_b128) and the transposing reads that
+//     give Q^T and dO^T (ds_read_b64_tr_b16) without bank conflicts.
+//   * dQ needs dS with one query per lane: dS^T goes to LDS (8-byte writes)
+//     and comes back through transposing reads. Each wave owns one 32-wide
+//     head-dim block of dQ, so its K operand for dQ += dS K is loaded once
+//     into registers; dQ is accumulated in fp32 with hardware float atomics,
+//     issued at the start of the next query tile so the per-tile wait only
+//     covers copies that had a whole tile's time to land.
+//   * Scheduling-group barriers interleave the MFMAs with the VALU work and
+//     the LDS operand reads of each phase.
 #include "fa_common.h"
 
 namespace fa {
@@ -72,45 +77,130 @@ __global__ __launch_bounds__(256) void fa_bwd_dq_kernel(
 }
 
 // ----------------------------------------------------------------- kernel 2
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
 struct BwdCfg {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 256;
   static constexpr int BNK = 128;          // keys per workgroup (32 per wave)
   static constexpr int BMQ = 64;           // queries per inner tile
-  static constexpr int QS = D + 8;         // row-major Q / dO stride (bf16)
-  static constexpr int TS = BMQ + 8;       // transposed Q / dO stride
-  static constexpr int SS = BNK + 8;       // dS stride
-  static constexpr int KTS = BNK + 8;      // K^T stride
-  static constexpr int KCH = D / 8;        // 16-byte chunks per row
-  static constexpr int UNITS = (BMQ / 4) * KCH;   // 4-row x 16-byte load units
+  static constexpr int RB = D * 2;         // bytes per Q / dO / K row in LDS
+  static constexpr int QTILE = BMQ * RB;   // 16 KiB (d=128)
+  static constexpr int KTILE = BNK * RB;   // 32 KiB (d=128)
+  static constexpr int SRB = BMQ * 2;      // bytes per dS^T row (one key)
+  static constexpr int STILE = BNK * SRB;  // 16 KiB
+  static constexpr int QLOADS = QTILE / 1024 / WAVES;   // 1 KiB copies per wave
+  static constexpr int KLOADS = KTILE / 1024 / WAVES;
+  static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int NQB = BMQ / 32;     // 32-query blocks per tile
-  static constexpr int DQ_BLOCKS = NQB * DB;      // 32x32 dQ blocks per tile
-  static constexpr int DQ_PER_WAVE = DQ_BLOCKS / WAVES;
-  static_assert(UNITS <= THREADS, "one load unit per thread at most");
-  static_assert(DQ_PER_WAVE * WAVES == DQ_BLOCKS, "dQ split");
+  static constexpr int DQ_QB = NQB * DB / WAVES;   // dQ query blocks per wave
+  static_assert(DQ_QB * WAVES == NQB * DB, "dQ split");
 };
 
+// Swizzled byte offset of 2-byte element (row, col) in a tile with R-byte
+// rows. Chunks of 16 bytes are XORed with a function of the row that is a
+// bijection over 16 consecutive rows (so a row-major operand read of 16 rows
+// hits 16 distinct bank groups) and whose top bits follow row%4 (so the 4
+// rows of a transposing read fall in 4 distinct 64-byte bank quarters).
+template <int R>
+__device__ __forceinline__ int sw_off(int row, int col) {
+  const int byte = col * 2;
+  int f;
+  if constexpr (R == 256) f = ((row & 3) << 2) | ((row >> 2) & 3);
+  else f = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  return row * R + ((((byte >> 4) ^ f)) << 4) + (byte & 15);
+}
+
+// Global -> LDS copies (global_load_lds: lane i writes LDS bytes
+// [M0 + size*i, +size)). They are issued from an asm statement so that the
+// compiler does not treat them as LDS stores that may alias the reads of the
+// other buffer (it would then wait for every copy before the next LDS read);
+// completion is awaited explicitly with wait_vmem() before the barrier that
+// publishes a buffer. The s_nop covers the M0-write -> LDS-DMA hazard.
+// The statements below write M0, which the compiler reserves; declaring the
+// clobber is what tells it so (it warns that a reserved register is listed,
+// hence the local pragma). Nothing else in this file uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+
+// This wave's share of the copy of LOADS*WAVES KiB of rows x D bf16 (rows past
+// N read row N-1) from global memory into a swizzled LDS tile: lane i of each
+// 1 KiB copy writes LDS bytes [16i, 16i+16), so it fetches the chunk the
+// swizzle puts there.
+template <int D, int LOADS>
+__device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, const uint8_t* lds,
+                                         int row0, int N, int w, int lane) {
+  constexpr int R = D * 2, RPL = 1024 / R, CPR = R / 16;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int lrow = (w * LOADS + i) * RPL;
+    const int row = lrow + lane / CPR;
+    const int pc = lane % CPR;
+    int f;
+    if constexpr (R == 256) f = ((row & 3) << 2) | ((row >> 2) & 3);
+    else f = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    const int c = pc ^ f;
+    const uint16_t* g = src + (size_t)min(row0 + row, N - 1) * D + c * 8;
+    lds_copy16(g, lds_addr(lds + lrow * R));
+  }
+}
+
+// Per-row statistics of one query tile into LDS (64 fp32 LSE, then 64 fp32
+// D; rows past N read row N-1): one 4-byte copy per lane of one wave.
+__device__ __forceinline__ void dma_stats(const float* __restrict__ lse, const float* __restrict__ dv,
+                                          const float* lds, int q0, int N, int lane) {
+  lds_copy4(lse + min(q0 + lane, N - 1), lds_addr(lds));
+  lds_copy4(dv + min(q0 + lane, N - 1), lds_addr(lds + 64));
+}
+
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // s_waitcnt vmcnt(0)
+}
+
+// Two transposing reads -> one bf16x8 MFMA operand: k-slot s of half h is
+// row 8*(s/4) + 4h + s%4 of the 16 rows read. o0 / o1 are the byte offsets
+// of the two halves (the swizzle depends on bits 2-3 of the row, so the half
+// 8 rows further has its own offset); base adds multiples of 16 rows.
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* base, int o0, int o1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base + o0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base + o1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fa_bwd_main_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dvec,
     float* __restrict__ dQacc, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     int BH, int N, int nkt, float c2, float scale, int xcd_group) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[C::BMQ * C::QS];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[C::BMQ * C::QS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * C::TS];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[D * C::TS];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[C::BMQ * C::SS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * C::KTS];
-  __shared__ float lse2s[C::BMQ];
-  __shared__ float Ds[C::BMQ];
+  constexpr int KS = C::KS, DB = C::DB, NQB = C::NQB, RB = C::RB, SRB = C::SRB;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[C::KTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds[2][C::QTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t o_lds[2][C::QTILE];   // dO tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[C::STILE];      // dS^T
+  __shared__ __attribute__((aligned(256))) float st_lds[2][2 * C::BMQ];   // LSE, D
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
   int head, rank;
@@ -127,8 +217,7 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(
   }
   // Causal: key tile 0 sees every query, the last one the fewest; issue the
   // heaviest first.
-  const int kt = rank;
-  const int k0 = kt * C::BNK;
+  const int k0 = rank * C::BNK;
   const int kk = k0 + 32 * w + l32;        // this lane's key
   const size_t off = (size_t)head * N * D;
   const uint16_t* Qh = Q + off;
@@ -137,186 +226,206 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(
   const float* Dh = Dvec + (size_t)head * N;
   float* dQh = dQacc + off;
 
-  // This lane's key row of K and V as B operands (k-slots = head dim).
-  bf16x8 kreg[D / 16], vreg[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const size_t o = (size_t)kk * D + ks * 16 + hi * 8;
-    u32x4 a = kk < N ? ld_global_16B(K + off + o) : zero_u32x4();
-    u32x4 b = kk < N ? ld_global_16B(V + off + o) : zero_u32x4();
-    kreg[ks] = __builtin_bit_cast(bf16x8, a);
-    vreg[ks] = __builtin_bit_cast(bf16x8, b);
-  }
-  // K^T of the whole key tile in LDS (B operand of dQ += dS K).
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const u32x4 a = __builtin_bit_cast(u32x4, kreg[ks]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t word = a[e >> 1];
-      const uint16_t h = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xffffu);
-      Kt[(ks * 16 + hi * 8 + e) * C::KTS + 32 * w + l32] = h;
-    }
-  }
-
-  f32x16 dkacc[C::DB], dvacc[C::DB];
-#pragma unroll
-  for (int i = 0; i < C::DB; ++i) {
-    dkacc[i] = zero16();
-    dvacc[i] = zero16();
-  }
-
   const int nqt = (N + C::BMQ - 1) / C::BMQ;
   const int it0 = CAUSAL ? (k0 / C::BMQ) : 0;
 
-  u32x4 qld[4], dld[4];
-  float lse_ld = 0.f, d_ld = 0.f;
-  const bool loader = tid < C::UNITS;
-  const int ucc = tid % C::KCH, ug = tid / C::KCH;   // chunk, 4-row group
+  // Copies: the K tile (for the dQ operands) and the first query tile.
+  dma_rows<D, C::KLOADS>(K + off, k_lds, k0, N, w, lane);
+  dma_rows<D, C::QLOADS>(Qh, q_lds[0], it0 * C::BMQ, N, w, lane);
+  dma_rows<D, C::QLOADS>(dOh, o_lds[0], it0 * C::BMQ, N, w, lane);
+  if (w == 0) dma_stats(LSEh, Dh, st_lds[0], it0 * C::BMQ, N, lane);
 
-  auto load_tile = [&](int it) {
-    const int qb0 = it * C::BMQ;
-    if (loader) {
+  // This lane's key row of K and V as B operands (k-slots = head dim).
+  bf16x8 kreg[KS], vreg[KS];
+  {
+    const size_t o = (size_t)min(kk, N - 1) * D + hi * 8;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int q = qb0 + 4 * ug + b;
-        qld[b] = q < N ? ld_global_16B(Qh + (size_t)q * D + ucc * 8) : zero_u32x4();
-        dld[b] = q < N ? ld_global_16B(dOh + (size_t)q * D + ucc * 8) : zero_u32x4();
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      kreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(K + off + o + ks * 16));
+      vreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(V + off + o + ks * 16));
     }
-    if (tid < C::BMQ) {
-      const int q = qb0 + tid;
-      lse_ld = q < N ? LSEh[q] * kLog2e : INFINITY;   // P = 0 for padded rows
-      d_ld = q < N ? Dh[q] : 0.f;
-    }
-  };
-  auto store_tile = [&]() {
-    if (loader) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int r = 4 * ug + b;
-        *reinterpret_cast<u32x4*>(Qs + r * C::QS + ucc * 8) = qld[b];
-        *reinterpret_cast<u32x4*>(dOs + r * C::QS + ucc * 8) = dld[b];
-      }
-      // Rows 4g..4g+3 (g = 4t + 2a + h) -> transposed positions 16t + 8h + 4a.
-      const int pos = 16 * (ug >> 2) + 8 * (ug & 1) + 4 * ((ug >> 1) & 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dw = e >> 1;
-        u32x2 pq, pd;
-        if (e & 1) {
-          pq = u32x2{pack_hi16(qld[0][dw], qld[1][dw]), pack_hi16(qld[2][dw], qld[3][dw])};
-          pd = u32x2{pack_hi16(dld[0][dw], dld[1][dw]), pack_hi16(dld[2][dw], dld[3][dw])};
-        } else {
-          pq = u32x2{pack_lo16(qld[0][dw], qld[1][dw]), pack_lo16(qld[2][dw], qld[3][dw])};
-          pd = u32x2{pack_lo16(dld[0][dw], dld[1][dw]), pack_lo16(dld[2][dw], dld[3][dw])};
-        }
-        *reinterpret_cast<u32x2*>(Qt + (ucc * 8 + e) * C::TS + pos) = pq;
-        *reinterpret_cast<u32x2*>(dOt + (ucc * 8 + e) * C::TS + pos) = pd;
-      }
-    }
-    if (tid < C::BMQ) {
-      lse2s[tid] = lse_ld;
-      Ds[tid] = d_ld;
-    }
-  };
-
-  if (it0 < nqt) {
-    load_tile(it0);
-    store_tile();
   }
 
-  for (int it = it0; it < nqt; ++it) {
-    __syncthreads();
-    if (it + 1 < nqt) load_tile(it + 1);
-    const int qbase = it * C::BMQ;
+  // dQ work of this wave: head-dim block dq_db, query blocks dq_qb0.. of each tile.
+  const int dq_db = w % DB;
+  const int dq_qb0 = (w / DB) * C::DQ_QB;
+  // Transposing-read lane offsets: lane (group g = lane/16, source s = lane%16)
+  // points at row 4*hi + s/4 (plus 16t + 8*half) and column 16*(g&1) + 4*(s&3)
+  // (plus 32*block) of a row-major tile.
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // ---- S = Q K^T and dP = dO V^T (one key per lane).
-    f32x16 sacc[C::NQB], pacc[C::NQB];
+  wait_vmem();
+  __syncthreads();
+
+  // Per-lane LDS offsets. The swizzles only look at bits 0-3 of the row, so
+  // whole 16-row (and 32-row) steps are plain immediate offsets: one register
+  // per (half, 32-column block) for transposing reads, one per k-step for
+  // the row-major operand reads.
+  int tq_off[2][DB];            // Q / dO tiles, transposing reads
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) tq_off[h][db] = sw_off<RB>(tr_row + 8 * h, 32 * db + tr_col);
+  int ts_off[2][C::DQ_QB];      // dS^T tile, transposing reads
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int x = 0; x < C::DQ_QB; ++x)
+      ts_off[h][x] = sw_off<SRB>(tr_row + 8 * h, 32 * (dq_qb0 + x) + tr_col);
+  int rq_off[KS];               // Q / dO tiles, row-major reads of row l32
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) rq_off[ks] = sw_off<RB>(l32, 16 * ks + 8 * hi);
+
+  // K operand of dQ += dS K for this wave's head-dim block: k-slots = keys.
+  bf16x8 ktreg[C::BNK / 16];
+#pragma unroll
+  for (int t = 0; t < C::BNK / 16; ++t)
+    ktreg[t] = tr_operand(k_lds + 16 * t * RB, sw_off<RB>(tr_row, 32 * dq_db + tr_col),
+                          sw_off<RB>(tr_row + 8, 32 * dq_db + tr_col));
+
+  f32x16 dkacc[DB], dvacc[DB], dqacc[C::DQ_QB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dkacc[i] = zero16();
+    dvacc[i] = zero16();
+  }
+#pragma unroll
+  for (int i = 0; i < C::DQ_QB; ++i) dqacc[i] = zero16();
+
+  // dQ partial sums of the previous tile -> fp32 atomics.
+  auto flush_dq = [&](int qbase) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < C::DQ_QB; ++x)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int q = qbase + 32 * (dq_qb0 + x) + 8 * (i >> 2) + 4 * hi + (i & 3);
+        if (q < N) unsafeAtomicAdd(dQh + (size_t)q * D + 32 * dq_db + l32, dqacc[x][i]);
+      }
+  };
+
+  for (int it = it0; it < nqt; ++it) {
+    // Buffers of this query tile (b) and of the next one (b ^ 1).
+    const int b = (it - it0) & 1;
+    const uint8_t* qt = q_lds[b];
+    const uint8_t* ot = o_lds[b];
+    const float* st = st_lds[b];
+    const int qbase = it * C::BMQ;
+    if (it + 1 < nqt) {
+      dma_rows<D, C::QLOADS>(Qh, q_lds[b ^ 1], qbase + C::BMQ, N, w, lane);
+      dma_rows<D, C::QLOADS>(dOh, o_lds[b ^ 1], qbase + C::BMQ, N, w, lane);
+      if (w == 0) dma_stats(LSEh, Dh, st_lds[b ^ 1], qbase + C::BMQ, N, lane);
+    }
+    if (it > it0) flush_dq(qbase - C::BMQ);
+
+    // ---- S = Q K^T and dP = dO V^T (one key per lane, 32 queries per block).
+    f32x16 sacc[NQB], pacc[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
       sacc[qb] = zero16();
       pacc[qb] = zero16();
+    }
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int o = (qb * 32 + l32) * C::QS + ks * 16 + hi * 8;
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + o);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dOs + o);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int o = 32 * qb * RB + rq_off[ks];
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + o);
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(ot + o);
         sacc[qb] = mfma_32x32x16(aq, kreg[ks], sacc[qb]);
         pacc[qb] = mfma_32x32x16(ad, vreg[ks], pacc[qb]);
       }
-    }
-    // ---- P = exp(S*scale - LSE) (base 2), dS = P o (dP - D).
+    // ---- P = exp2(S*scale*log2e - LSE*log2e), dS = P o (dP - D), packed to
+    // bf16 right away (k-slot order of the dV / dK B operands: 16 queries per
+    // step t, registers 8*(t&1) .. +7 of block t/2).
+    const bool masked = (CAUSAL && qbase < k0 + C::BNK - 1) || qbase + C::BMQ > N ||
+                        k0 + C::BNK > N;
+    bf16x8 pbv[C::BMQ / 16], sbv[C::BMQ / 16];
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qi = qb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        const int q = qbase + qi;
-        float p = fast_exp2(fmaf(sacc[qb][i], c2, -lse2s[qi]));
-        if ((CAUSAL && kk > q) || kk >= N) p = 0.f;
-        sacc[qb][i] = p;
-        pacc[qb][i] = p * (pacc[qb][i] - Ds[qi]);
+      for (int half = 0; half < 2; ++half) {
+        float pv[8], dv8[8];
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g4 = 2 * half + g2;
+          const int ql = 32 * qb + 8 * g4 + 4 * hi;     // first of 4 consecutive queries
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + ql);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + C::BMQ + ql);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g4 + e;
+            float p = fast_exp2(fmaf(sacc[qb][i], c2, -lse4[e] * kLog2e));
+            if (masked) {
+              const int q = qbase + ql + e;
+              if ((CAUSAL && kk > q) || kk >= N || q >= N) p = 0.f;
+            }
+            pv[4 * g2 + e] = p;
+            dv8[4 * g2 + e] = p * (pacc[qb][i] - d4[e]);
+          }
+        }
+        const int t = 2 * qb + half;
+        pbv[t] = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        sbv[t] = pack_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
       }
     // ---- dV^T += dO^T P and dK^T += Q^T dS (k-slots = queries).
 #pragma unroll
     for (int t = 0; t < C::BMQ / 16; ++t) {
-      const int r0 = (t & 1) * 8;
-      const f32x16& p = sacc[t >> 1];
-      const f32x16& s = pacc[t >> 1];
-      const bf16x8 pb = pack_bf16x8(p[r0], p[r0 + 1], p[r0 + 2], p[r0 + 3], p[r0 + 4],
-                                    p[r0 + 5], p[r0 + 6], p[r0 + 7]);
-      const bf16x8 sb = pack_bf16x8(s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4],
-                                    s[r0 + 5], s[r0 + 6], s[r0 + 7]);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const int o = (db * 32 + l32) * C::TS + 16 * t + 8 * hi;
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dOt + o);
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qt + o);
-        dvacc[db] = mfma_32x32x16(ad, pb, dvacc[db]);
-        dkacc[db] = mfma_32x32x16(aq, sb, dkacc[db]);
+      for (int db = 0; db < DB; ++db) {
+        dvacc[db] = mfma_32x32x16(tr_operand(ot + 16 * t * RB, tq_off[0][db], tq_off[1][db]), pbv[t], dvacc[db]);
+        dkacc[db] = mfma_32x32x16(tr_operand(qt + 16 * t * RB, tq_off[0][db], tq_off[1][db]), sbv[t], dkacc[db]);
       }
     }
-    // ---- dS (bf16) to LDS, one query per row.
+    // ---- dS^T (bf16) to LDS: row = this lane's key, 4 consecutive queries
+    // (one half of a packed operand) per write.
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const int qi = qb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        const uint32_t pr = pack_bf16x2(pacc[qb][i], pacc[qb][i + 1]);
-        dSs[qi * C::SS + 32 * w + l32] = (uint16_t)(pr & 0xffffu);
-        dSs[(qi + 1) * C::SS + 32 * w + l32] = (uint16_t)(pr >> 16);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const u32x4 w4 = __builtin_bit_cast(u32x4, sbv[2 * qb + (g4 >> 1)]);
+        const u32x2 v = {w4[2 * (g4 & 1)], w4[2 * (g4 & 1) + 1]};
+        *reinterpret_cast<u32x2*>(s_lds + sw_off<SRB>(32 * w + l32, 32 * qb + 8 * g4 + 4 * hi)) = v;
       }
-    __syncthreads();
-    // ---- dQ += dS K over the 128 keys of this workgroup (fp32 atomics).
+    {
+      constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+      // S / dP MFMAs each with one operand read; the dV / dK MFMAs each with
+      // two transposing reads and the exp / dS / packing work.
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
 #pragma unroll
-    for (int x = 0; x < C::DQ_PER_WAVE; ++x) {
-      const int bi = w + C::WAVES * x;
-      const int qb = bi % C::NQB, db = bi / C::NQB;
-      f32x16 acc = zero16();
+      for (int i = 0; i < 2 * KS * NQB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * (C::BMQ / 16) * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
+      }
+    }
+    __syncthreads();
+    // ---- dQ (this wave's head-dim block) = dS K over the 128 keys.
+#pragma unroll
+    for (int x = 0; x < C::DQ_QB; ++x) {
+      dqacc[x] = zero16();
 #pragma unroll
       for (int t = 0; t < C::BNK / 16; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            dSs + (qb * 32 + l32) * C::SS + 16 * t + 8 * hi);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(
-            Kt + (db * 32 + l32) * C::KTS + 16 * t + 8 * hi);
-        acc = mfma_32x32x16(a, b, acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = qbase + qb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        if (q < N) unsafeAtomicAdd(dQh + (size_t)q * D + db * 32 + l32, acc[i]);
+        const bf16x8 a = tr_operand(s_lds + 16 * t * SRB, ts_off[0][x], ts_off[1][x]);
+        dqacc[x] = mfma_32x32x16(a, ktreg[t], dqacc[x]);
       }
     }
-    if (it + 1 < nqt) store_tile();
+    wait_vmem();
+    __syncthreads();
   }
+  flush_dq((nqt - 1) * C::BMQ);
 
   // ---- dK = scale * dK^T, dV = dV^T (one key per lane; 4 consecutive d).
   if (kk < N) {
     uint16_t* dkrow = dK + off + (size_t)kk * D;
     uint16_t* dvrow = dV + off + (size_t)kk * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = db * 32 + 8 * g4 + 4 * hi;
