@@ -54,6 +54,22 @@ def bwd_bytes(w):
     return 5 * n * w.d * 2 + 4 * n + 8 * n + 3 * n * w.d * 2
 
 
+def recorded_traffic(workload_idx, launch):
+    """HBM bytes per launch from the committed counter record, or None when the
+    kernel sources changed since the counters were taken (hash mismatch)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{launch}_workload{workload_idx}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    csrc = os.path.join(ROOT, "exact_io_aware_12_amd", "csrc")
+    srcs = "".join(open(os.path.join(csrc, f)).read()
+                   for f in ("fa_common.h", "fa_fwd.hip", "fa_bwd.hip"))
+    if hashlib.sha256(srcs.encode()).hexdigest()[:16] != rec.get("sources_sha256_16"):
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
+
+
 def cpu_baseline(w, inp, budget_s):
     """Time the oracle (as it stands) on a bounded sample of heads."""
     import numpy as np
@@ -162,12 +178,15 @@ def main():
     bwd_tf = (w.bwd_flops() / (b_avg * 1e-3) / 1e12) if w.backward else None
     if w.backward and b_avg > f_avg:
         dom = {"launch": "fa_bwd (kernels fa_bwd_pre, fa_bwd_main, fa_bwd_dq back to back)",
-               "achieved": bwd_tf, "avg_ms": b_avg}
+               "achieved": bwd_tf, "avg_ms": b_avg,
+               "traffic": recorded_traffic(args.workload, "fa_bwd")}
     else:
-        dom = {"launch": "fa_fwd (kernel fa_fwd_kernel)", "achieved": fwd_tf, "avg_ms": f_avg}
+        dom = {"launch": "fa_fwd (kernel fa_fwd_kernel)", "achieved": fwd_tf, "avg_ms": f_avg,
+               "traffic": recorded_traffic(args.workload, "fa_fwd")}
     roofline = {"bound": "mfma", "achieved": round(dom["achieved"], 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(dom["achieved"] / PEAK_BF16_TFLOPS, 4),
+                "traffic": dom["traffic"],
                 "kernel": dom["launch"], "avg_launch_ms": round(dom["avg_ms"], 4)}
 
     if args.copy_calib_mib > 0:
