@@ -81,18 +81,28 @@ __device__ __forceinline__ int v_off(int row, int col) {
 // Slack (log2 units) before the running max is moved.
 constexpr float kRescaleSlack = 8.f;
 
+// Max over the NB*16 score registers of a lane as a tree of 3-input maxima
+// (v_maximum3_f32): 32 values in 16 instructions.
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 template <int NB>
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB]) {
-  float r[NB * 4];
+  constexpr int n = NB * 16;
+  float r[n];
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      r[kb * 4 + g] = vmax(vmax(s[kb][4 * g], s[kb][4 * g + 1]), vmax(s[kb][4 * g + 2], s[kb][4 * g + 3]));
+    for (int i = 0; i < 16; ++i) r[kb * 16 + i] = s[kb][i];
+  int m = n;
 #pragma unroll
-  for (int w = NB * 4; w > 1; w >>= 1)
+  for (int level = 0; level < 6; ++level) {
+    if (m == 1) break;
+    int k = 0, i = 0;
 #pragma unroll
-    for (int i = 0; i < w / 2; ++i) r[i] = vmax(r[i], r[i + w / 2]);
+    for (; i + 2 < m; i += 3) r[k++] = vmax3(r[i], r[i + 1], r[i + 2]);
+    if (m - i == 2) r[k++] = vmax(r[i], r[i + 1]);
+    else if (m - i == 1) r[k++] = r[i];
+    m = k;
+  }
   return r[0];
 }
 template <int NB>
@@ -124,36 +134,72 @@ __device__ __forceinline__ float tile_sum(const f32x16 (&s)[NB]) {
   return r[0];
 }
 
-// Issue this wave's share of the DMA of one K or V tile (rows kb0..kb0+BN-1;
-// rows past N read row N-1) into an LDS buffer: LOADS x 1 KiB per wave. Lane
-// i of a load writes LDS bytes [16i, 16i+16) of its 1 KiB, so each lane
-// fetches the global chunk that the swizzle places there.
+// Global -> LDS copies (global_load_lds_dwordx4: lane i writes LDS bytes
+// [M0 + 16i, +16)), in the scalar-base form: the tile's base address is one
+// SGPR pair and each lane adds a constant 32-bit byte offset, so a tile copy
+// costs no per-lane address arithmetic. Issued from an asm statement (it
+// writes M0, hence the clobber and the local pragma); the s_nop covers the
+// M0-write -> LDS-DMA hazard. Completion is awaited with wait_dma() before
+// the barrier that publishes a buffer.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+
+// Byte offset (within a tile) of the global chunk that lane `lane` of this
+// wave's copy i fetches: lane l writes physical 16-byte chunk l % (RB/16) of
+// row lrow + l / (RB/16), so it reads the logical chunk the swizzle puts
+// there. Rows are relative to the tile's first key.
+template <int D, bool IS_V>
+__device__ __forceinline__ int dma_row(int w, int i, int lane) {
+  using C = FwdCfg<D>;
+  return (w * C::LOADS + i) * C::ROWS_PER_LOAD + lane / (C::RB / 16);
+}
+template <int D, bool IS_V>
+__device__ __forceinline__ int dma_col(int row, int lane) {
+  using C = FwdCfg<D>;
+  const int pc = lane % (C::RB / 16);                         // physical 16-byte chunk
+  if constexpr (!IS_V) {
+    int c;
+    if constexpr (D == 128) c = pc ^ (row & 15);
+    else c = pc ^ ((row >> 1) & 7);
+    return c * 8;
+  } else {
+    const int pb = pc >> 2;
+    int lb;
+    if constexpr (D == 128) lb = pb ^ (row & 3);
+    else lb = pb ^ ((row >> 1) & 1);
+    return lb * 32 + (pc & 3) * 8;
+  }
+}
+
+// This wave's share (LOADS x 1 KiB) of the copy of one K or V tile (keys
+// kb0 .. kb0+BN-1). `off` holds the per-lane byte offsets for a full tile;
+// on the ragged last tile, rows past N read row N-1 instead.
 template <int D, bool IS_V>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint8_t* lds,
-                                         int kb0, int N, int w, int lane) {
+                                         int kb0, int N, int w, int lane,
+                                         const uint32_t (&off)[FwdCfg<D>::LOADS]) {
   using C = FwdCfg<D>;
+  const uint16_t* base = src + (size_t)kb0 * D;
+  if (kb0 + C::BN <= N) {
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int lrow = (w * C::LOADS + i) * C::ROWS_PER_LOAD;   // first row of this 1 KiB
-    const int row = lrow + lane / (C::RB / 16);
-    const int pc = lane % (C::RB / 16);                       // physical 16-byte chunk
-    int col;                                                  // logical first column
-    if constexpr (!IS_V) {
-      int c;
-      if constexpr (D == 128) c = pc ^ (row & 15);
-      else c = pc ^ ((row >> 1) & 7);
-      col = c * 8;
-    } else {
-      const int pb = pc >> 2;
-      int lb;
-      if constexpr (D == 128) lb = pb ^ (row & 3);
-      else lb = pb ^ ((row >> 1) & 1);
-      col = lb * 32 + (pc & 3) * 8;
+    for (int i = 0; i < C::LOADS; ++i)
+      lds_copy16(base, off[i], lds_addr_of(lds + (w * C::LOADS + i) * 1024));
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int row = dma_row<D, IS_V>(w, i, lane);
+      const int r = min(row, N - 1 - kb0);
+      const uint32_t o = (uint32_t)(r * D + dma_col<D, IS_V>(row, lane)) * 2u;
+      lds_copy16(base, o, lds_addr_of(lds + (w * C::LOADS + i) * 1024));
     }
-    const int key = min(kb0 + row, N - 1);
-    const uint16_t* g = src + (size_t)key * D + col;
-    __builtin_amdgcn_global_load_lds((const GLB_AS void*)g,
-                                     (LDS_AS void*)(lds + lrow * C::RB), 16, 0, 0);
   }
 }
 
@@ -214,10 +260,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Tiles this wave computes: 0 .. ntw-1 (causal waves stop at the diagonal).
   const int ntw = CAUSAL ? min(nt, (min(N, qw + 32) + C::BN - 1) / C::BN) : nt;
 
+  // Per-lane byte offsets of the K and V tile copies (constant across tiles).
+  uint32_t koffd[C::LOADS], voffd[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int rk = dma_row<D, false>(w, i, lane);
+    koffd[i] = (uint32_t)(rk * D + dma_col<D, false>(rk, lane)) * 2u;
+    const int rv = dma_row<D, true>(w, i, lane);
+    voffd[i] = (uint32_t)(rv * D + dma_col<D, true>(rv, lane)) * 2u;
+  }
+
   // Prologue DMA: K0, V0, K1.
-  dma_tile<D, false>(Kh, k_lds0, 0, N, w, lane);
-  dma_tile<D, true>(Vh, v_lds0, 0, N, w, lane);
-  if (nt > 1) dma_tile<D, false>(Kh, k_lds1, C::BN, N, w, lane);
+  dma_tile<D, false>(Kh, k_lds0, 0, N, w, lane, koffd);
+  dma_tile<D, true>(Vh, v_lds0, 0, N, w, lane, voffd);
+  if (nt > 1) dma_tile<D, false>(Kh, k_lds1, C::BN, N, w, lane, koffd);
 
   // Q rows of this lane as B operands (rows past N read row N-1; never stored).
   bf16x8 qreg[C::KS];
@@ -329,7 +385,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int i = 0; i < 16; ++i) scur[kb][i] = fast_exp2(fmaf(scur[kb][i], c2, nm));
     }
-    l_run += tile_sum<C::NB>(scur);
     // O^T += V^T P^T: 16 keys per MFMA; k-slot s of half h is key
     // 8*(s/4) + 4h + s%4 of the 16, both in P^T (accumulator rows) and in
     // the V^T operand (two transposing reads of 4 keys each).
@@ -348,6 +403,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         oacc[db] = mfma_32x32x16(a, pb, oacc[db]);
       }
     }
+    // The row sum is taken over the fp32 p (a sum of the bf16-rounded p would
+    // move the LSE by up to 2^-9 on rows with few keys).
+    l_run += tile_sum<C::NB>(scur);
     // Instruction order for this block (one wave issues in order, so MFMA
     // work only overlaps VALU work that sits between the MFMAs, and LDS
     // latency is only hidden by reads issued several MFMAs ahead): the S^T
@@ -388,8 +446,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint8_t* const k_next = P ? k_lds0 : k_lds1;   // K_{j+1}
     uint8_t* const v_this = P ? v_lds1 : v_lds0;   // V_j
     uint8_t* const v_next = P ? v_lds0 : v_lds1;   // refilled with V_{j+1}
-    if (j + 2 < nt) dma_tile<D, false>(Kh, k_this, (j + 2) * C::BN, N, w, lane);
-    if (j + 1 < nt) dma_tile<D, true>(Vh, v_next, (j + 1) * C::BN, N, w, lane);
+    if (j + 2 < nt) dma_tile<D, false>(Kh, k_this, (j + 2) * C::BN, N, w, lane, koffd);
+    if (j + 1 < nt) dma_tile<D, true>(Vh, v_next, (j + 1) * C::BN, N, w, lane, voffd);
     f32x16 (&scur)[C::NB] = sacc[P];
     f32x16 (&snext)[C::NB] = sacc[P ^ 1];
     if (j < ntw) {
