@@ -203,6 +203,18 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint8
   }
 }
 
+// Copy i of this wave's share of a tile, branch-free: `full` / `ragged` are
+// the per-lane offsets for a full tile and for the ragged last tile (the
+// only tile that can be ragged).
+template <int D>
+__device__ __forceinline__ void dma_part(const uint16_t* __restrict__ src, uint8_t* lds,
+                                         int kb0, int N, int w, int i, uint32_t full,
+                                         uint32_t ragged) {
+  using C = FwdCfg<D>;
+  const uint32_t o = (kb0 + C::BN <= N) ? full : ragged;
+  lds_copy16(src + (size_t)kb0 * D, o, lds_addr_of(lds + (w * C::LOADS + i) * 1024));
+}
+
 __device__ __forceinline__ void wait_dma() {
   // s_waitcnt vmcnt(0): this wave's outstanding global->LDS copies are done.
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -269,6 +281,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int rv = dma_row<D, true>(w, i, lane);
     voffd[i] = (uint32_t)(rv * D + dma_col<D, true>(rv, lane)) * 2u;
   }
+  // The same for the last tile when it is ragged (rows past N read row N-1).
+  uint32_t koffr[C::LOADS], voffr[C::LOADS];
+  {
+    const int kl = (nt - 1) * C::BN;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int rk = dma_row<D, false>(w, i, lane);
+      koffr[i] = (uint32_t)(min(rk, N - 1 - kl) * D + dma_col<D, false>(rk, lane)) * 2u;
+      const int rv = dma_row<D, true>(w, i, lane);
+      voffr[i] = (uint32_t)(min(rv, N - 1 - kl) * D + dma_col<D, true>(rv, lane)) * 2u;
+    }
+  }
 
   // Prologue DMA: K0, V0, K1.
   dma_tile<D, false>(Kh, k_lds0, 0, N, w, lane, koffd);
@@ -308,18 +332,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = -INFINITY;   // running (reference) max of this lane's row, log2 domain
   float l_run = 0.f;         // running sum over this lane's half of the keys
 
-  auto scores = [&](f32x16 (&s)[C::NB], const uint8_t* kt) __attribute__((always_inline)) {
+  auto scores = [&](f32x16 (&s)[C::NB], const uint8_t* kt, auto&& hook) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < C::NB; ++kb) s[kb] = zero16();
     // k-step outer: consecutive MFMAs alternate between the independent
     // accumulators of the 32-key blocks instead of waiting on one chain.
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+    for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < C::NB; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * C::RB + koff[ks]);
         s[kb] = mfma_32x32x16(a, qreg[ks], s[kb]);
       }
+      if ((ks + 1) % (C::KS / C::LOADS) == 0) hook((ks + 1) / (C::KS / C::LOADS) - 1);
+    }
   };
 
   f32x16 sacc[2][C::NB];   // scores of tiles j (parity of j) and j+1
@@ -368,8 +394,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // O^T += V^T P^T of this tile, so the scheduler can interleave MFMA and
   // VALU work of one wave.
   auto tile_body = [&](f32x16 (&scur)[C::NB], f32x16 (&snext)[C::NB], const uint8_t* k_next,
-                       const uint8_t* v_this) __attribute__((always_inline)) {
-    scores(snext, k_next);
+                       const uint8_t* v_this, auto&& kcopy, auto&& vcopy) __attribute__((always_inline)) {
+    scores(snext, k_next, kcopy);
     // A row with no admissible key so far keeps m = -inf (all its scores
     // are -inf): subtract 0 so that p = 0.
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
@@ -402,6 +428,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = mfma_32x32x16(a, pb, oacc[db]);
       }
+      if ((t + 1) % ((C::BN / 16) / C::LOADS) == 0) vcopy((t + 1) / ((C::BN / 16) / C::LOADS) - 1);
     }
     // The row sum is taken over the fp32 p (a sum of the bf16-rounded p would
     // move the LSE by up to 2^-9 on rows with few keys).
@@ -432,7 +459,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   wait_dma();
   __syncthreads();
   if (ntw > 0) {
-    scores(sacc[0], k_lds0);
+    scores(sacc[0], k_lds0, [](int) {});
     tile_stats(sacc[0], 0);
   }
   __syncthreads();   // K buffer 0 is refilled by the first tile step
@@ -446,16 +473,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint8_t* const k_next = P ? k_lds0 : k_lds1;   // K_{j+1}
     uint8_t* const v_this = P ? v_lds1 : v_lds0;   // V_j
     uint8_t* const v_next = P ? v_lds0 : v_lds1;   // refilled with V_{j+1}
-    if (j + 2 < nt) dma_tile<D, false>(Kh, k_this, (j + 2) * C::BN, N, w, lane, koffd);
-    if (j + 1 < nt) dma_tile<D, true>(Vh, v_next, (j + 1) * C::BN, N, w, lane, voffd);
+    // Copies of K_{j+2} and V_{j+1}, spread over the MFMA stream of the
+    // tile step; near the end they repeat the last tile (in bounds, unused).
+    const int kc0 = min(j + 2, nt - 1) * C::BN, vc0 = min(j + 1, nt - 1) * C::BN;
+    auto kcopy = [&](int i) __attribute__((always_inline)) {
+      dma_part<D>(Kh, k_this, kc0, N, w, i, koffd[i], koffr[i]);
+    };
+    auto vcopy = [&](int i) __attribute__((always_inline)) {
+      dma_part<D>(Vh, v_next, vc0, N, w, i, voffd[i], voffr[i]);
+    };
     f32x16 (&scur)[C::NB] = sacc[P];
     f32x16 (&snext)[C::NB] = sacc[P ^ 1];
     if (j < ntw) {
       // The next tile's scores are computed even on this wave's last tile
       // (then from whatever the other K buffer holds, and never used): one
       // code path keeps the register allocation of the loop simple.
-      tile_body(scur, snext, k_next, v_this);
+      tile_body(scur, snext, k_next, v_this, kcopy, vcopy);
       if (j + 1 < ntw) tile_stats(snext, (j + 1) * C::BN);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) { kcopy(i); vcopy(i); }
     }
     wait_dma();
     __syncthreads();
