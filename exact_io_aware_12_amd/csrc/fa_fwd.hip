@@ -60,6 +60,8 @@ struct FwdCfg {
   static constexpr int NB = BN / 32;           // 32-key score blocks per tile
   static constexpr int DB = D / 32;            // 32-wide output blocks
   static constexpr int KS = D / 16;            // k-steps of S^T
+  // One K or V tile copy follows each k-step of S^T (2*LOADS copies a step).
+  static_assert(KS == 2 * LOADS, "one tile copy per k-step");
 };
 
 // Byte offset of (row, 16-byte chunk c) of a K tile in LDS. The XOR makes the
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * C::RB + koff[ks]);
         s[kb] = mfma_32x32x16(a, qreg[ks], s[kb]);
       }
-      if ((ks + 1) % (C::KS / C::LOADS) == 0) hook((ks + 1) / (C::KS / C::LOADS) - 1);
+      hook(ks);
     }
   };
 
@@ -394,8 +396,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // O^T += V^T P^T of this tile, so the scheduler can interleave MFMA and
   // VALU work of one wave.
   auto tile_body = [&](f32x16 (&scur)[C::NB], f32x16 (&snext)[C::NB], const uint8_t* k_next,
-                       const uint8_t* v_this, auto&& kcopy, auto&& vcopy) __attribute__((always_inline)) {
-    scores(snext, k_next, kcopy);
+                       const uint8_t* v_this, auto&& copy) __attribute__((always_inline)) {
+    scores(snext, k_next, copy);
     // A row with no admissible key so far keeps m = -inf (all its scores
     // are -inf): subtract 0 so that p = 0.
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
@@ -428,7 +430,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = mfma_32x32x16(a, pb, oacc[db]);
       }
-      if ((t + 1) % ((C::BN / 16) / C::LOADS) == 0) vcopy((t + 1) / ((C::BN / 16) / C::LOADS) - 1);
     }
     // The row sum is taken over the fp32 p (a sum of the bf16-rounded p would
     // move the LSE by up to 2^-9 on rows with few keys).
@@ -473,14 +474,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint8_t* const k_next = P ? k_lds0 : k_lds1;   // K_{j+1}
     uint8_t* const v_this = P ? v_lds1 : v_lds0;   // V_j
     uint8_t* const v_next = P ? v_lds0 : v_lds1;   // refilled with V_{j+1}
-    // Copies of K_{j+2} and V_{j+1}, spread over the MFMA stream of the
-    // tile step; near the end they repeat the last tile (in bounds, unused).
+    // Copies of K_{j+2} and V_{j+1} (copy c: K part c/2 for even c, V part
+    // c/2 for odd c), one after each k-step of the S^T MFMAs: spread out so
+    // they do not stall instruction issue as a burst would, and all in the
+    // first half of the step so they complete before the closing barrier.
+    // Near the end they repeat the last tile (in bounds, unused).
     const int kc0 = min(j + 2, nt - 1) * C::BN, vc0 = min(j + 1, nt - 1) * C::BN;
-    auto kcopy = [&](int i) __attribute__((always_inline)) {
-      dma_part<D>(Kh, k_this, kc0, N, w, i, koffd[i], koffr[i]);
-    };
-    auto vcopy = [&](int i) __attribute__((always_inline)) {
-      dma_part<D>(Vh, v_next, vc0, N, w, i, voffd[i], voffr[i]);
+    auto copy = [&](int c) __attribute__((always_inline)) {
+      const int i = c >> 1;
+      if (c & 1) dma_part<D>(Vh, v_next, vc0, N, w, i, voffd[i], voffr[i]);
+      else dma_part<D>(Kh, k_this, kc0, N, w, i, koffd[i], koffr[i]);
     };
     f32x16 (&scur)[C::NB] = sacc[P];
     f32x16 (&snext)[C::NB] = sacc[P ^ 1];
@@ -488,11 +491,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // The next tile's scores are computed even on this wave's last tile
       // (then from whatever the other K buffer holds, and never used): one
       // code path keeps the register allocation of the loop simple.
-      tile_body(scur, snext, k_next, v_this, kcopy, vcopy);
+      tile_body(scur, snext, k_next, v_this, copy);
       if (j + 1 < ntw) tile_stats(snext, (j + 1) * C::BN);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::LOADS; ++i) { kcopy(i); vcopy(i); }
+      for (int c = 0; c < 2 * C::LOADS; ++c) copy(c);
     }
     wait_dma();
     __syncthreads();
