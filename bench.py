@@ -33,8 +33,8 @@ METRIC = "attention fwd/bwd TFLOP/s (bf16, d=128) and % of MI355X bf16 MFMA peak
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
