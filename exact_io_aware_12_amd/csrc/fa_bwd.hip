@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dvec,
     float* __restrict__ dQacc, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    int BH, int N, int nkt, float c2, float scale, int xcd_group) {
+    int BH, int N, int nunits, float c2, float scale, int xcd_group) {
   using C = BwdCfg<D>;
   constexpr int KS = C::KS, DB = C::DB, NQB = C::NQB, RB = C::RB, SRB = C::SRB;
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[C::KTILE];
@@ -203,48 +203,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
-  int head, rank;
+  // Workgroup -> (head, work unit). Causal: unit u covers the key tiles u and
+  // nkt-1-u: first key tile u with the query tiles in descending order, then
+  // key tile nkt-1-u with them in ascending order. Every unit then costs the
+  // same number of query-tile steps, and since the units of a head start
+  // together, they all work on the same query tile (or two) at any time, so
+  // the fp32 dQ rows being accumulated and the Q / dO tiles being read stay
+  // in the XCD's L2. Non-causal: one key tile per unit, ascending.
+  int head, unit;
   {
     const int b = blockIdx.x;
     if (xcd_group > 0) {
+      // Workgroups are dispatched round-robin over the 8 XCDs; XCD x gets the
+      // heads [x*G, (x+1)*G), head-major.
       const int x = b & 7, s = b >> 3;
-      head = x * xcd_group + s % xcd_group;
-      rank = s / xcd_group;
+      head = x * xcd_group + s / nunits;
+      unit = s % nunits;
     } else {
-      head = b % BH;
-      rank = b / BH;
+      head = b / nunits;
+      unit = b % nunits;
     }
   }
-  // Causal: key tile 0 sees every query, the last one the fewest; issue the
-  // heaviest first.
-  const int k0 = rank * C::BNK;
-  const int kk = k0 + 32 * w + l32;        // this lane's key
   const size_t off = (size_t)head * N * D;
   const uint16_t* Qh = Q + off;
   const uint16_t* dOh = dO + off;
   const float* LSEh = LSE + (size_t)head * N;
   const float* Dh = Dvec + (size_t)head * N;
   float* dQh = dQacc + off;
-
   const int nqt = (N + C::BMQ - 1) / C::BMQ;
-  const int it0 = CAUSAL ? (k0 / C::BMQ) : 0;
-
-  // Copies: the K tile (for the dQ operands) and the first query tile.
-  dma_rows<D, C::KLOADS>(K + off, k_lds, k0, N, w, lane);
-  dma_rows<D, C::QLOADS>(Qh, q_lds[0], it0 * C::BMQ, N, w, lane);
-  dma_rows<D, C::QLOADS>(dOh, o_lds[0], it0 * C::BMQ, N, w, lane);
-  if (w == 0) dma_stats(LSEh, Dh, st_lds[0], it0 * C::BMQ, N, lane);
-
-  // This lane's key row of K and V as B operands (k-slots = head dim).
-  bf16x8 kreg[KS], vreg[KS];
-  {
-    const size_t o = (size_t)min(kk, N - 1) * D + hi * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(K + off + o + ks * 16));
-      vreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(V + off + o + ks * 16));
-    }
-  }
 
   // dQ work of this wave: head-dim block dq_db, query blocks dq_qb0.. of each tile.
   const int dq_db = w % DB;
@@ -254,9 +240,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // (plus 32*block) of a row-major tile.
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  wait_vmem();
-  __syncthreads();
 
   // Per-lane LDS offsets. The swizzles only look at bits 0-3 of the row, so
   // whole 16-row (and 32-row) steps are plain immediate offsets: one register
@@ -277,167 +260,209 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) rq_off[ks] = sw_off<RB>(l32, 16 * ks + 8 * hi);
 
-  // K operand of dQ += dS K for this wave's head-dim block: k-slots = keys.
-  bf16x8 ktreg[C::BNK / 16];
-#pragma unroll
-  for (int t = 0; t < C::BNK / 16; ++t)
-    ktreg[t] = tr_operand(k_lds + 16 * t * RB, sw_off<RB>(tr_row, 32 * dq_db + tr_col),
-                          sw_off<RB>(tr_row + 8, 32 * dq_db + tr_col));
-
+  bf16x8 kreg[KS], vreg[KS];          // this lane's key row of K and V (B operands)
+  bf16x8 ktreg[C::BNK / 16];          // K operand of dQ += dS K (k-slots = keys)
   f32x16 dkacc[DB], dvacc[DB], dqacc[C::DQ_QB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    dkacc[i] = zero16();
-    dvacc[i] = zero16();
-  }
-#pragma unroll
-  for (int i = 0; i < C::DQ_QB; ++i) dqacc[i] = zero16();
+  int k0 = 0, kk = 0;                 // first key of the tile, this lane's key
 
-  // dQ partial sums of the previous tile -> fp32 atomics.
+  // dQ partial sums of a tile -> fp32 atomics. A full tile takes the
+  // branch-free form (uniform base + constant per-lane offsets); only a tile
+  // that crosses N needs per-element predicates.
+  const int dq_lane = (32 * dq_qb0 + 4 * hi) * D + 32 * dq_db + l32;
   auto flush_dq = [&](int qbase) __attribute__((always_inline)) {
+    if (qbase + C::BMQ <= N) {
+      float* const base = dQh + (size_t)qbase * D;
 #pragma unroll
-    for (int x = 0; x < C::DQ_QB; ++x)
+      for (int x = 0; x < C::DQ_QB; ++x)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = qbase + 32 * (dq_qb0 + x) + 8 * (i >> 2) + 4 * hi + (i & 3);
-        if (q < N) unsafeAtomicAdd(dQh + (size_t)q * D + 32 * dq_db + l32, dqacc[x][i]);
-      }
+        for (int i = 0; i < 16; ++i)
+          unsafeAtomicAdd(base + dq_lane + (32 * x + 8 * (i >> 2) + (i & 3)) * D, dqacc[x][i]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < C::DQ_QB; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = qbase + 32 * (dq_qb0 + x) + 8 * (i >> 2) + 4 * hi + (i & 3);
+          if (q < N) unsafeAtomicAdd(dQh + (size_t)q * D + 32 * dq_db + l32, dqacc[x][i]);
+        }
+    }
   };
 
-  for (int it = it0; it < nqt; ++it) {
-    // Buffers of this query tile (b) and of the next one (b ^ 1).
-    const int b = (it - it0) & 1;
-    const uint8_t* qt = q_lds[b];
-    const uint8_t* ot = o_lds[b];
-    const float* st = st_lds[b];
-    const int qbase = it * C::BMQ;
-    if (it + 1 < nqt) {
-      dma_rows<D, C::QLOADS>(Qh, q_lds[b ^ 1], qbase + C::BMQ, N, w, lane);
-      dma_rows<D, C::QLOADS>(dOh, o_lds[b ^ 1], qbase + C::BMQ, N, w, lane);
-      if (w == 0) dma_stats(LSEh, Dh, st_lds[b ^ 1], qbase + C::BMQ, N, lane);
-    }
-    if (it > it0) flush_dq(qbase - C::BMQ);
+  const int nkt_ = (N + C::BNK - 1) / C::BNK;
+  const int nparts = (CAUSAL && 2 * unit + 1 != nkt_) ? 2 : 1;
+  for (int part = 0; part < nparts; ++part) {
+    const int kt = part == 0 ? unit : nkt_ - 1 - unit;
+    k0 = kt * C::BNK;
+    kk = k0 + 32 * w + l32;
+    // Query tiles it_lo .. nqt-1 (causal: from the one holding key k0), in
+    // descending order in the first part of a causal unit.
+    const bool rev = CAUSAL && part == 0;
+    const int it_lo = CAUSAL ? (k0 / C::BMQ) : 0;
+    const int nsteps = nqt - it_lo;
+    auto tile_at = [&](int step) __attribute__((always_inline)) {
+      return rev ? nqt - 1 - step : it_lo + step;
+    };
 
-    // ---- S = Q K^T and dP = dO V^T (one key per lane, 32 queries per block).
-    f32x16 sacc[NQB], pacc[NQB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      sacc[qb] = zero16();
-      pacc[qb] = zero16();
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int o = 32 * qb * RB + rq_off[ks];
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + o);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(ot + o);
-        sacc[qb] = mfma_32x32x16(aq, kreg[ks], sacc[qb]);
-        pacc[qb] = mfma_32x32x16(ad, vreg[ks], pacc[qb]);
-      }
-    // ---- P = exp2(S*scale*log2e - LSE*log2e), dS = P o (dP - D), packed to
-    // bf16 right away (k-slot order of the dV / dK B operands: 16 queries per
-    // step t, registers 8*(t&1) .. +7 of block t/2).
-    const bool masked = (CAUSAL && qbase < k0 + C::BNK - 1) || qbase + C::BMQ > N ||
-                        k0 + C::BNK > N;
-    bf16x8 pbv[C::BMQ / 16], sbv[C::BMQ / 16];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float pv[8], dv8[8];
-#pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) {
-          const int g4 = 2 * half + g2;
-          const int ql = 32 * qb + 8 * g4 + 4 * hi;     // first of 4 consecutive queries
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + ql);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + C::BMQ + ql);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g4 + e;
-            float p = fast_exp2(fmaf(sacc[qb][i], c2, -lse4[e] * kLog2e));
-            if (masked) {
-              const int q = qbase + ql + e;
-              if ((CAUSAL && kk > q) || kk >= N || q >= N) p = 0.f;
-            }
-            pv[4 * g2 + e] = p;
-            dv8[4 * g2 + e] = p * (pacc[qb][i] - d4[e]);
-          }
-        }
-        const int t = 2 * qb + half;
-        pbv[t] = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-        sbv[t] = pack_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
-      }
-    // ---- dV^T += dO^T P and dK^T += Q^T dS (k-slots = queries).
-#pragma unroll
-    for (int t = 0; t < C::BMQ / 16; ++t) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dvacc[db] = mfma_32x32x16(tr_operand(ot + 16 * t * RB, tq_off[0][db], tq_off[1][db]), pbv[t], dvacc[db]);
-        dkacc[db] = mfma_32x32x16(tr_operand(qt + 16 * t * RB, tq_off[0][db], tq_off[1][db]), sbv[t], dkacc[db]);
-      }
-    }
-    // ---- dS^T (bf16) to LDS: row = this lane's key, 4 consecutive queries
-    // (one half of a packed operand) per write.
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const u32x4 w4 = __builtin_bit_cast(u32x4, sbv[2 * qb + (g4 >> 1)]);
-        const u32x2 v = {w4[2 * (g4 & 1)], w4[2 * (g4 & 1) + 1]};
-        *reinterpret_cast<u32x2*>(s_lds + sw_off<SRB>(32 * w + l32, 32 * qb + 8 * g4 + 4 * hi)) = v;
-      }
+    // Copies: the K tile (for the dQ operands) and the first query tile.
+    dma_rows<D, C::KLOADS>(K + off, k_lds, k0, N, w, lane);
+    dma_rows<D, C::QLOADS>(Qh, q_lds[0], tile_at(0) * C::BMQ, N, w, lane);
+    dma_rows<D, C::QLOADS>(dOh, o_lds[0], tile_at(0) * C::BMQ, N, w, lane);
+    if (w == 0) dma_stats(LSEh, Dh, st_lds[0], tile_at(0) * C::BMQ, N, lane);
     {
-      constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
-      // S / dP MFMAs each with one operand read; the dV / dK MFMAs each with
-      // two transposing reads and the exp / dS / packing work.
-      __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+      const size_t o = (size_t)min(kk, N - 1) * D + hi * 8;
 #pragma unroll
-      for (int i = 0; i < 2 * KS * NQB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 2 * (C::BMQ / 16) * DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
-      }
-    }
-    __syncthreads();
-    // ---- dQ (this wave's head-dim block) = dS K over the 128 keys.
-#pragma unroll
-    for (int x = 0; x < C::DQ_QB; ++x) {
-      dqacc[x] = zero16();
-#pragma unroll
-      for (int t = 0; t < C::BNK / 16; ++t) {
-        const bf16x8 a = tr_operand(s_lds + 16 * t * SRB, ts_off[0][x], ts_off[1][x]);
-        dqacc[x] = mfma_32x32x16(a, ktreg[t], dqacc[x]);
+      for (int ks = 0; ks < KS; ++ks) {
+        kreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(K + off + o + ks * 16));
+        vreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(V + off + o + ks * 16));
       }
     }
     wait_vmem();
     __syncthreads();
-  }
-  flush_dq((nqt - 1) * C::BMQ);
+#pragma unroll
+    for (int t = 0; t < C::BNK / 16; ++t)
+      ktreg[t] = tr_operand(k_lds + 16 * t * RB, sw_off<RB>(tr_row, 32 * dq_db + tr_col),
+                            sw_off<RB>(tr_row + 8, 32 * dq_db + tr_col));
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      dkacc[i] = zero16();
+      dvacc[i] = zero16();
+    }
 
-  // ---- dK = scale * dK^T, dV = dV^T (one key per lane; 4 consecutive d).
-  if (kk < N) {
-    uint16_t* dkrow = dK + off + (size_t)kk * D;
-    uint16_t* dvrow = dV + off + (size_t)kk * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hi;
-        const f32x16& a = dkacc[db];
-        const f32x16& b = dvacc[db];
-        u32x2 pk = {pack_bf16x2(a[4 * g4] * scale, a[4 * g4 + 1] * scale),
-                    pack_bf16x2(a[4 * g4 + 2] * scale, a[4 * g4 + 3] * scale)};
-        u32x2 pv = {pack_bf16x2(b[4 * g4], b[4 * g4 + 1]),
-                    pack_bf16x2(b[4 * g4 + 2], b[4 * g4 + 3])};
-        *reinterpret_cast<u32x2*>(dkrow + d0) = pk;
-        *reinterpret_cast<u32x2*>(dvrow + d0) = pv;
+    for (int step = 0; step < nsteps; ++step) {
+      // Buffers of this query tile (b) and of the next one (b ^ 1).
+      const int b = step & 1;
+      const uint8_t* qt = q_lds[b];
+      const uint8_t* ot = o_lds[b];
+      const float* st = st_lds[b];
+      const int qbase = tile_at(step) * C::BMQ;
+      if (step + 1 < nsteps) {
+        const int qn = tile_at(step + 1) * C::BMQ;
+        dma_rows<D, C::QLOADS>(Qh, q_lds[b ^ 1], qn, N, w, lane);
+        dma_rows<D, C::QLOADS>(dOh, o_lds[b ^ 1], qn, N, w, lane);
+        if (w == 0) dma_stats(LSEh, Dh, st_lds[b ^ 1], qn, N, lane);
       }
+      if (step > 0) flush_dq(tile_at(step - 1) * C::BMQ);
+      // ---- S = Q K^T and dP = dO V^T (one key per lane, 32 queries per block).
+      f32x16 sacc[NQB], pacc[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        sacc[qb] = zero16();
+        pacc[qb] = zero16();
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const int o = 32 * qb * RB + rq_off[ks];
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + o);
+          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(ot + o);
+          sacc[qb] = mfma_32x32x16(aq, kreg[ks], sacc[qb]);
+          pacc[qb] = mfma_32x32x16(ad, vreg[ks], pacc[qb]);
+        }
+      // ---- P = exp2(S*scale*log2e - LSE*log2e), dS = P o (dP - D), packed to
+      // bf16 right away (k-slot order of the dV / dK B operands: 16 queries per
+      // step t, registers 8*(t&1) .. +7 of block t/2).
+      const bool masked = (CAUSAL && qbase < k0 + C::BNK - 1) || qbase + C::BMQ > N ||
+                          k0 + C::BNK > N;
+      bf16x8 pbv[C::BMQ / 16], sbv[C::BMQ / 16];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float pv[8], dv8[8];
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const int g4 = 2 * half + g2;
+            const int ql = 32 * qb + 8 * g4 + 4 * hi;     // first of 4 consecutive queries
+            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + ql);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + C::BMQ + ql);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * g4 + e;
+              float p = fast_exp2(fmaf(sacc[qb][i], c2, -lse4[e] * kLog2e));
+              if (masked) {
+                const int q = qbase + ql + e;
+                if ((CAUSAL && kk > q) || kk >= N || q >= N) p = 0.f;
+              }
+              pv[4 * g2 + e] = p;
+              dv8[4 * g2 + e] = p * (pacc[qb][i] - d4[e]);
+            }
+          }
+          const int t = 2 * qb + half;
+          pbv[t] = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+          sbv[t] = pack_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
+        }
+      // ---- dV^T += dO^T P and dK^T += Q^T dS (k-slots = queries).
+#pragma unroll
+      for (int t = 0; t < C::BMQ / 16; ++t) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dvacc[db] = mfma_32x32x16(tr_operand(ot + 16 * t * RB, tq_off[0][db], tq_off[1][db]), pbv[t], dvacc[db]);
+          dkacc[db] = mfma_32x32x16(tr_operand(qt + 16 * t * RB, tq_off[0][db], tq_off[1][db]), sbv[t], dkacc[db]);
+        }
+      }
+      // ---- dS^T (bf16) to LDS: row = this lane's key, 4 consecutive queries
+      // (one half of a packed operand) per write.
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const u32x4 w4 = __builtin_bit_cast(u32x4, sbv[2 * qb + (g4 >> 1)]);
+          const u32x2 v = {w4[2 * (g4 & 1)], w4[2 * (g4 & 1) + 1]};
+          *reinterpret_cast<u32x2*>(s_lds + sw_off<SRB>(32 * w + l32, 32 * qb + 8 * g4 + 4 * hi)) = v;
+        }
+      {
+        constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+        // S / dP MFMAs each with one operand read; the dV / dK MFMAs each with
+        // two transposing reads and the exp / dS / packing work.
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * KS * NQB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * (C::BMQ / 16) * DB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
+        }
+      }
+      __syncthreads();
+      // ---- dQ (this wave's head-dim block) = dS K over the 128 keys.
+#pragma unroll
+      for (int x = 0; x < C::DQ_QB; ++x) {
+        dqacc[x] = zero16();
+#pragma unroll
+        for (int t = 0; t < C::BNK / 16; ++t) {
+          const bf16x8 a = tr_operand(s_lds + 16 * t * SRB, ts_off[0][x], ts_off[1][x]);
+          dqacc[x] = mfma_32x32x16(a, ktreg[t], dqacc[x]);
+        }
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+    flush_dq(tile_at(nsteps - 1) * C::BMQ);
+
+    // ---- dK = scale * dK^T, dV = dV^T (one key per lane; 4 consecutive d).
+    if (kk < N) {
+      uint16_t* dkrow = dK + off + (size_t)kk * D;
+      uint16_t* dvrow = dV + off + (size_t)kk * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * hi;
+          const f32x16& a = dkacc[db];
+          const f32x16& b = dvacc[db];
+          u32x2 pk = {pack_bf16x2(a[4 * g4] * scale, a[4 * g4 + 1] * scale),
+                      pack_bf16x2(a[4 * g4 + 2] * scale, a[4 * g4 + 3] * scale)};
+          u32x2 pv = {pack_bf16x2(b[4 * g4], b[4 * g4 + 1]),
+                      pack_bf16x2(b[4 * g4 + 2], b[4 * g4 + 3])};
+          *reinterpret_cast<u32x2*>(dkrow + d0) = pk;
+          *reinterpret_cast<u32x2*>(dvrow + d0) = pv;
+        }
+    }
   }
 }
 
@@ -456,10 +481,11 @@ static hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_
   }
   {
     const int nkt = (N + C::BNK - 1) / C::BNK;
+    const int nunits = CAUSAL ? (nkt + 1) / 2 : nkt;   // causal: key tiles u and nkt-1-u
     const int xcd_group = (BH % 8 == 0) ? BH / 8 : 0;
-    dim3 grid((unsigned)(nkt * BH));
+    dim3 grid((unsigned)(nunits * BH));
     hipLaunchKernelGGL((fa_bwd_main_kernel<D, CAUSAL>), grid, dim3(C::THREADS), 0, stream,
-                       q, k, v, dout, lse, dvec, dqacc, dk, dv, BH, N, nkt, scale * kLog2e,
+                       q, k, v, dout, lse, dvec, dqacc, dk, dv, BH, N, nunits, scale * kLog2e,
                        scale, xcd_group);
   }
   {
