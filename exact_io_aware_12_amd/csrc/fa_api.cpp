@@ -14,8 +14,8 @@ hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         bool causal, hipStream_t stream);
 hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* o, const uint16_t* dout, const float* lse,
-                        uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dqacc, float* dvec,
-                        int BH, int N, int d, float scale, bool causal, hipStream_t stream);
+                        uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec, int BH, int N,
+                        int d, float scale, bool causal, hipStream_t stream);
 }  // namespace fa
 
 namespace {
@@ -56,7 +56,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (check_shape(B, H, N, d) != FA_OK) return 0;
   const size_t rows = (size_t)B * H * N;
-  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+  return round256(rows * sizeof(float));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -72,15 +72,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
-  const size_t rows = (size_t)B * H * N;
-  float* dqacc = static_cast<float*>(workspace);
-  float* dvec = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         round256(rows * d * sizeof(float)));
+  float* dvec = static_cast<float*>(workspace);
   hipError_t e = fa::bwd_dispatch(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
       static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
-      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dqacc, dvec, B * H, N, d, scale,
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dvec, B * H, N, d, scale,
       causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

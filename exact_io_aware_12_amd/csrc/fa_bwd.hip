@@ -6,32 +6,41 @@
 // dS = P o (dP - D) (times the scale), dQ += dS K, dK += dS^T Q. The row
 // statistic D_i = sum_j P_ij dP_ij is a sum over the WHOLE row (it equals
 // dO_i . O_i); taken per tile it would not be the gradient, so it is computed
-// once per row before the tile loop.
+// once per row before the tile loops.
 //
 // Three kernels on the caller's stream:
-//   1. fa_bwd_pre:   D_i = dO_i . O_i (fp32) and zero the fp32 dQ accumulator.
-//   2. fa_bwd_main:  one workgroup per 128-key tile (4 wave64s x 32 keys, one
-//      wave per SIMD); the loop runs over 64-query tiles (outer loop over K/V,
-//      inner over Q, so dK and dV stay in registers for the whole loop).
-//   3. fa_bwd_dq:    dQ = scale * accumulator, rounded to bf16.
+//   1. fa_bwd_pre:   D_i = dO_i . O_i (fp32).
+//   2. fa_bwd_dkdv:  dK and dV. One workgroup per key tile pair (4 wave64s x
+//      32 keys, one wave per SIMD); the loop runs over 64-query tiles (outer
+//      loop over K/V, inner over Q, so dK and dV stay in registers).
+//   3. fa_bwd_dq:    dQ. One workgroup per 128-query tile (4 wave64s x 32
+//      queries, two workgroups per CU); the loop runs over 64-key tiles and
+//      recomputes S and dP (inner loop over K/V, so dQ stays in registers).
+// Splitting dQ from dK/dV costs two extra matmuls per tile pair (S and dP are
+// computed in both kernels: 7 instead of 5), and buys the removal of every
+// cross-workgroup accumulation: on this multi-XCD device, device-scope fp32
+// atomics into a dQ accumulator are performed past the L2 and cost more than
+// the recomputation.
 //
-// gfx950 mapping of the main kernel (32x32x16 bf16 MFMAs, fp32 accumulate):
-//   * S = Q K^T and dP = dO V^T are computed with one key per lane (the B
-//     operands K and V of this wave's 32 keys live in registers), so P and dS
-//     sit in registers in exactly the layout the B operand of
-//     dV^T += dO^T P and dK^T += Q^T dS needs (k-slots are queries).
-//   * Q and dO tiles go from HBM/L2 straight into LDS (global_load_lds_dwordx4,
+// gfx950 mapping (32x32x16 bf16 MFMAs, fp32 accumulate):
+//   * dK/dV kernel: S = Q K^T and dP = dO V^T are computed with one key per
+//     lane (the B operands K and V of this wave's 32 keys live in registers),
+//     so P and dS sit in registers in exactly the layout the B operand of
+//     dV^T += dO^T P and dK^T += Q^T dS needs (k-slots are queries). Q and dO
+//     tiles go from HBM/L2 straight into LDS (global_load_lds_dwordx4,
 //     double-buffered) in one XOR swizzle that serves both the row-major
 //     operand reads of S and dP (ds_read_b128) and the transposing reads that
 //     give Q^T and dO^T (ds_read_b64_tr_b16) without bank conflicts.
-//   * dQ needs dS with one query per lane: dS^T goes to LDS (8-byte writes)
-//     and comes back through transposing reads. Each wave owns one 32-wide
-//     head-dim block of dQ, so its K operand for dQ += dS K is loaded once
-//     into registers; dQ is accumulated in fp32 with hardware float atomics,
-//     issued at the start of the next query tile so the per-tile wait only
-//     covers copies that had a whole tile's time to land.
+//   * dQ kernel: the transposed form of the forward pass, one query per lane:
+//     S^T = K Q^T and dP^T = V dO^T (Q and dO rows in registers as B
+//     operands, K and V rows from LDS), P^T and dS^T element-wise with the
+//     lane's own LSE and D, and dQ^T += K^T dS^T with dS^T fed from the
+//     accumulator registers as the B operand and K^T from transposing reads
+//     of the same swizzled K tile.
 //   * Scheduling-group barriers interleave the MFMAs with the VALU work and
 //     the LDS operand reads of each phase.
+#include <type_traits>
+
 #include "fa_common.h"
 
 namespace fa {
@@ -40,7 +49,7 @@ namespace fa {
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-    float* __restrict__ Dvec, float* __restrict__ dQacc, long long rows) {
+    float* __restrict__ Dvec, long long rows) {
   constexpr int TPR = D / 8;            // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;        // rows per block
   const int tid = threadIdx.x;
@@ -55,25 +64,10 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(
       acc += __uint_as_float(a[e] << 16) * __uint_as_float(b[e] << 16);
       acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(b[e] & 0xffff0000u);
     }
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(dQacc + row * D + c * 8) = z;
-    *reinterpret_cast<f32x4*>(dQacc + row * D + c * 8 + 4) = z;
   }
 #pragma unroll
   for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (row < rows && c == 0) Dvec[row] = acc;
-}
-
-// ----------------------------------------------------------------- kernel 3
-__global__ __launch_bounds__(256) void fa_bwd_dq_kernel(
-    const float* __restrict__ dQacc, uint16_t* __restrict__ dQ, long long n8, float scale) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(dQacc + i * 8);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(dQacc + i * 8 + 4);
-  u32x4 o = {pack_bf16x2(a[0] * scale, a[1] * scale), pack_bf16x2(a[2] * scale, a[3] * scale),
-             pack_bf16x2(b[0] * scale, b[1] * scale), pack_bf16x2(b[2] * scale, b[3] * scale)};
-  *reinterpret_cast<u32x4*>(dQ + i * 8) = o;
 }
 
 // ----------------------------------------------------------------- kernel 2
@@ -87,18 +81,12 @@ struct BwdCfg {
   static constexpr int THREADS = 256;
   static constexpr int BNK = 128;          // keys per workgroup (32 per wave)
   static constexpr int BMQ = 64;           // queries per inner tile
-  static constexpr int RB = D * 2;         // bytes per Q / dO / K row in LDS
+  static constexpr int RB = D * 2;         // bytes per Q / dO row in LDS
   static constexpr int QTILE = BMQ * RB;   // 16 KiB (d=128)
-  static constexpr int KTILE = BNK * RB;   // 32 KiB (d=128)
-  static constexpr int SRB = BMQ * 2;      // bytes per dS^T row (one key)
-  static constexpr int STILE = BNK * SRB;  // 16 KiB
   static constexpr int QLOADS = QTILE / 1024 / WAVES;   // 1 KiB copies per wave
-  static constexpr int KLOADS = KTILE / 1024 / WAVES;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int NQB = BMQ / 32;     // 32-query blocks per tile
-  static constexpr int DQ_QB = NQB * DB / WAVES;   // dQ query blocks per wave
-  static_assert(DQ_QB * WAVES == NQB * DB, "dQ split");
 };
 
 // Swizzled byte offset of 2-byte element (row, col) in a tile with R-byte
@@ -184,18 +172,16 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* base, int o0, int o1
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_main_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dvec,
-    float* __restrict__ dQacc, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     int BH, int N, int nunits, float c2, float scale, int xcd_group) {
   using C = BwdCfg<D>;
-  constexpr int KS = C::KS, DB = C::DB, NQB = C::NQB, RB = C::RB, SRB = C::SRB;
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[C::KTILE];
+  constexpr int KS = C::KS, DB = C::DB, NQB = C::NQB, RB = C::RB;
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds[2][C::QTILE];
   __shared__ __attribute__((aligned(1024))) uint8_t o_lds[2][C::QTILE];   // dO tiles
-  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[C::STILE];      // dS^T
   __shared__ __attribute__((aligned(256))) float st_lds[2][2 * C::BMQ];   // LSE, D
 
   const int tid = threadIdx.x;
@@ -208,8 +194,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // key tile nkt-1-u with them in ascending order. Every unit then costs the
   // same number of query-tile steps, and since the units of a head start
   // together, they all work on the same query tile (or two) at any time, so
-  // the fp32 dQ rows being accumulated and the Q / dO tiles being read stay
-  // in the XCD's L2. Non-causal: one key tile per unit, ascending.
+  // the Q / dO tiles being read stay in the XCD's L2. Non-causal: one key
+  // tile per unit, ascending.
   int head, unit;
   {
     const int b = blockIdx.x;
@@ -229,12 +215,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint16_t* dOh = dO + off;
   const float* LSEh = LSE + (size_t)head * N;
   const float* Dh = Dvec + (size_t)head * N;
-  float* dQh = dQacc + off;
   const int nqt = (N + C::BMQ - 1) / C::BMQ;
 
-  // dQ work of this wave: head-dim block dq_db, query blocks dq_qb0.. of each tile.
-  const int dq_db = w % DB;
-  const int dq_qb0 = (w / DB) * C::DQ_QB;
   // Transposing-read lane offsets: lane (group g = lane/16, source s = lane%16)
   // points at row 4*hi + s/4 (plus 16t + 8*half) and column 16*(g&1) + 4*(s&3)
   // (plus 32*block) of a row-major tile.
@@ -250,43 +232,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int db = 0; db < DB; ++db) tq_off[h][db] = sw_off<RB>(tr_row + 8 * h, 32 * db + tr_col);
-  int ts_off[2][C::DQ_QB];      // dS^T tile, transposing reads
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int x = 0; x < C::DQ_QB; ++x)
-      ts_off[h][x] = sw_off<SRB>(tr_row + 8 * h, 32 * (dq_qb0 + x) + tr_col);
   int rq_off[KS];               // Q / dO tiles, row-major reads of row l32
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) rq_off[ks] = sw_off<RB>(l32, 16 * ks + 8 * hi);
 
   bf16x8 kreg[KS], vreg[KS];          // this lane's key row of K and V (B operands)
-  bf16x8 ktreg[C::BNK / 16];          // K operand of dQ += dS K (k-slots = keys)
-  f32x16 dkacc[DB], dvacc[DB], dqacc[C::DQ_QB];
+  f32x16 dkacc[DB], dvacc[DB];
   int k0 = 0, kk = 0;                 // first key of the tile, this lane's key
-
-  // dQ partial sums of a tile -> fp32 atomics. A full tile takes the
-  // branch-free form (uniform base + constant per-lane offsets); only a tile
-  // that crosses N needs per-element predicates.
-  const int dq_lane = (32 * dq_qb0 + 4 * hi) * D + 32 * dq_db + l32;
-  auto flush_dq = [&](int qbase) __attribute__((always_inline)) {
-    if (qbase + C::BMQ <= N) {
-      float* const base = dQh + (size_t)qbase * D;
-#pragma unroll
-      for (int x = 0; x < C::DQ_QB; ++x)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          unsafeAtomicAdd(base + dq_lane + (32 * x + 8 * (i >> 2) + (i & 3)) * D, dqacc[x][i]);
-    } else {
-#pragma unroll
-      for (int x = 0; x < C::DQ_QB; ++x)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = qbase + 32 * (dq_qb0 + x) + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (q < N) unsafeAtomicAdd(dQh + (size_t)q * D + 32 * dq_db + l32, dqacc[x][i]);
-        }
-    }
-  };
 
   const int nkt_ = (N + C::BNK - 1) / C::BNK;
   const int nparts = (CAUSAL && 2 * unit + 1 != nkt_) ? 2 : 1;
@@ -303,8 +255,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       return rev ? nqt - 1 - step : it_lo + step;
     };
 
-    // Copies: the K tile (for the dQ operands) and the first query tile.
-    dma_rows<D, C::KLOADS>(K + off, k_lds, k0, N, w, lane);
+    // Copies: the first query tile.
     dma_rows<D, C::QLOADS>(Qh, q_lds[0], tile_at(0) * C::BMQ, N, w, lane);
     dma_rows<D, C::QLOADS>(dOh, o_lds[0], tile_at(0) * C::BMQ, N, w, lane);
     if (w == 0) dma_stats(LSEh, Dh, st_lds[0], tile_at(0) * C::BMQ, N, lane);
@@ -318,10 +269,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     wait_vmem();
     __syncthreads();
-#pragma unroll
-    for (int t = 0; t < C::BNK / 16; ++t)
-      ktreg[t] = tr_operand(k_lds + 16 * t * RB, sw_off<RB>(tr_row, 32 * dq_db + tr_col),
-                            sw_off<RB>(tr_row + 8, 32 * dq_db + tr_col));
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
       dkacc[i] = zero16();
@@ -341,7 +288,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dma_rows<D, C::QLOADS>(dOh, o_lds[b ^ 1], qn, N, w, lane);
         if (w == 0) dma_stats(LSEh, Dh, st_lds[b ^ 1], qn, N, lane);
       }
-      if (step > 0) flush_dq(tile_at(step - 1) * C::BMQ);
       // ---- S = Q K^T and dP = dO V^T (one key per lane, 32 queries per block).
       f32x16 sacc[NQB], pacc[NQB];
 #pragma unroll
@@ -401,16 +347,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           dkacc[db] = mfma_32x32x16(tr_operand(qt + 16 * t * RB, tq_off[0][db], tq_off[1][db]), sbv[t], dkacc[db]);
         }
       }
-      // ---- dS^T (bf16) to LDS: row = this lane's key, 4 consecutive queries
-      // (one half of a packed operand) per write.
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const u32x4 w4 = __builtin_bit_cast(u32x4, sbv[2 * qb + (g4 >> 1)]);
-          const u32x2 v = {w4[2 * (g4 & 1)], w4[2 * (g4 & 1) + 1]};
-          *reinterpret_cast<u32x2*>(s_lds + sw_off<SRB>(32 * w + l32, 32 * qb + 8 * g4 + 4 * hi)) = v;
-        }
       {
         constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
         // S / dP MFMAs each with one operand read; the dV / dK MFMAs each with
@@ -428,21 +364,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
         }
       }
-      __syncthreads();
-      // ---- dQ (this wave's head-dim block) = dS K over the 128 keys.
-#pragma unroll
-      for (int x = 0; x < C::DQ_QB; ++x) {
-        dqacc[x] = zero16();
-#pragma unroll
-        for (int t = 0; t < C::BNK / 16; ++t) {
-          const bf16x8 a = tr_operand(s_lds + 16 * t * SRB, ts_off[0][x], ts_off[1][x]);
-          dqacc[x] = mfma_32x32x16(a, ktreg[t], dqacc[x]);
-        }
-      }
       wait_vmem();
       __syncthreads();
     }
-    flush_dq(tile_at(nsteps - 1) * C::BMQ);
 
     // ---- dK = scale * dK^T, dV = dV^T (one key per lane; 4 consecutive d).
     if (kk < N) {
@@ -466,49 +390,218 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// ----------------------------------------------------------------- kernel 3
+template <int D>
+struct DqCfg {
+  static constexpr int BM = 128;              // queries per workgroup (32 per wave)
+  static constexpr int THREADS = 256;         // 4 waves
+  static constexpr int BN = 64;               // keys per tile
+  static constexpr int RB = D * 2;            // bytes per K / V row in LDS
+  static constexpr int TILE = BN * RB;        // 16 KiB (d=128)
+  static constexpr int LOADS = TILE / 1024 / 4;   // 1 KiB copies per wave
+  static constexpr int NB = BN / 32;          // 32-key blocks per tile
+  static constexpr int DB = D / 32;           // 32-wide head-dim blocks
+  static constexpr int KS = D / 16;           // k-steps of S^T and dP^T
+};
+
+// dQ_i = scale * sum_j dS_ij K_j for one 128-query tile per workgroup.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    uint16_t* __restrict__ dQ, int BH, int N, int ntq, float c2, float scale, int xcd_group) {
+  using C = DqCfg<D>;
+  constexpr int KS = C::KS, DB = C::DB, NB = C::NB, RB = C::RB;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[2][C::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // Workgroup -> (head, query tile): heaviest causal tiles first, the
+  // workgroups of a head on one XCD (as in the forward pass).
+  int head, rank;
+  {
+    const int b = blockIdx.x;
+    if (xcd_group > 0) {
+      const int x = b & 7, s = b >> 3;
+      head = x * xcd_group + s % xcd_group;
+      rank = s / xcd_group;
+    } else {
+      head = b % BH;
+      rank = b / BH;
+    }
+  }
+  const int qt = CAUSAL ? (ntq - 1 - rank) : rank;
+  const int q0 = qt * C::BM;
+  const int qw = q0 + 32 * w;          // first query row of this wave
+  const int qrow = qw + l32;           // this lane's query row
+  const int qc = min(qrow, N - 1);     // rows past N compute with row N-1 (never stored)
+  const size_t off = (size_t)head * N * D;
+  const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
+  const int nt = (kend + C::BN - 1) / C::BN;
+  // Key tiles this wave computes: 0 .. ntw-1 (causal waves stop at the diagonal).
+  const int ntw = CAUSAL ? min(nt, (min(N, qw + 32) + C::BN - 1) / C::BN) : nt;
+
+  dma_rows<D, C::LOADS>(K + off, k_lds[0], 0, N, w, lane);
+  dma_rows<D, C::LOADS>(V + off, v_lds[0], 0, N, w, lane);
+
+  // This lane's Q and dO rows as B operands (k-slots = head dim), and its
+  // row statistics: LSE in log2 units and D.
+  bf16x8 qreg[KS], doreg[KS];
+  {
+    const size_t o = off + (size_t)qc * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(Q + o + ks * 16));
+      doreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(dO + o + ks * 16));
+    }
+  }
+  const float nlse2 = -LSE[(size_t)head * N + qc] * kLog2e;
+  const float drow = Dvec[(size_t)head * N + qc];
+
+  // Per-lane LDS offsets (the swizzle only looks at bits 0-3 of the row, so
+  // 16- and 32-row steps are immediates): row-major reads of row l32 (K and
+  // V operands of S^T and dP^T), transposing reads (K^T operand of dQ^T).
+  int rk_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) rk_off[ks] = sw_off<RB>(l32, 16 * ks + 8 * hi);
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int tk_off[2][DB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) tk_off[h][db] = sw_off<RB>(tr_row + 8 * h, 32 * db + tr_col);
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dqacc[i] = zero16();
+
+  // One key tile, one 32-key block at a time (one S^T / dP^T pair live):
+  // S^T = K Q^T and dP^T = V dO^T (one query per lane), the exponent
+  // x = S^T*scale*log2e - LSE*log2e, set to -inf for masked keys (a small
+  // branch taken only on tiles that cross the diagonal or N; one code path
+  // keeps the register allocation within budget), P^T = exp2(x),
+  // dS^T = P^T o (dP^T - D) packed per 16-key group t (registers
+  // 8*(t&1) .. +7 of the block: k-slot s of half h is key 8*(s/4) + 4h + s%4
+  // of the group, the order of the transposing K reads), dQ^T += K^T dS^T.
+  auto tile = [&](const uint8_t* kt, const uint8_t* vt, int kbase, bool masked)
+                  __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      f32x16 sa = zero16(), pa = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int o = kb * 32 * RB + rk_off[ks];
+        sa = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(kt + o), qreg[ks], sa);
+        pa = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(vt + o), doreg[ks], pa);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sa[i] = fmaf(sa[i], c2, nlse2);
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
+          sa[i] = (key >= N || (CAUSAL && key > qrow)) ? -INFINITY : sa[i];
+        }
+      }
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        const int t = 2 * kb + th;
+        float ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ds[e] = fast_exp2(sa[8 * th + e]) * (pa[8 * th + e] - drow);
+        const bf16x8 sb = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dqacc[db] = mfma_32x32x16(tr_operand(kt + 16 * t * RB, tk_off[0][db], tk_off[1][db]),
+                                    sb, dqacc[db]);
+      }
+    }
+  };
+
+  wait_vmem();
+  __syncthreads();
+
+  for (int j = 0; j < nt; ++j) {
+    const int b = j & 1;
+    if (j + 1 < nt) {
+      dma_rows<D, C::LOADS>(K + off, k_lds[b ^ 1], (j + 1) * C::BN, N, w, lane);
+      dma_rows<D, C::LOADS>(V + off, v_lds[b ^ 1], (j + 1) * C::BN, N, w, lane);
+    }
+    if (j < ntw) {
+      const int kbase = j * C::BN;
+      const bool masked = (CAUSAL && kbase + C::BN - 1 > qw) || kbase + C::BN > N;
+      tile(k_lds[b], v_lds[b], kbase, masked);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- dQ = scale * dQ^T (one query per lane; 4 consecutive d per store).
+  if (qrow < N) {
+    uint16_t* qrow_p = dQ + off + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * hi;
+        u32x2 pr = {pack_bf16x2(dqacc[db][4 * g4 + 0] * scale, dqacc[db][4 * g4 + 1] * scale),
+                    pack_bf16x2(dqacc[db][4 * g4 + 2] * scale, dqacc[db][4 * g4 + 3] * scale)};
+        *reinterpret_cast<u32x2*>(qrow_p + d0) = pr;
+      }
+  }
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const uint16_t* o, const uint16_t* dout, const float* lse,
-                             uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dqacc,
-                             float* dvec, int BH, int N, float scale, hipStream_t stream) {
-  using C = BwdCfg<D>;
+                             uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec, int BH,
+                             int N, float scale, hipStream_t stream) {
   const long long rows = (long long)BH * N;
+  const int xcd_group = (BH % 8 == 0) ? BH / 8 : 0;
   {
     constexpr int RPB = 256 / (D / 8);
     dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), grid, dim3(256), 0, stream, o, dout, dvec,
-                       dqacc, rows);
+    hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), grid, dim3(256), 0, stream, o, dout, dvec, rows);
   }
   {
+    using C = BwdCfg<D>;
     const int nkt = (N + C::BNK - 1) / C::BNK;
     const int nunits = CAUSAL ? (nkt + 1) / 2 : nkt;   // causal: key tiles u and nkt-1-u
-    const int xcd_group = (BH % 8 == 0) ? BH / 8 : 0;
     dim3 grid((unsigned)(nunits * BH));
-    hipLaunchKernelGGL((fa_bwd_main_kernel<D, CAUSAL>), grid, dim3(C::THREADS), 0, stream,
-                       q, k, v, dout, lse, dvec, dqacc, dk, dv, BH, N, nunits, scale * kLog2e,
-                       scale, xcd_group);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(C::THREADS), 0, stream,
+                       q, k, v, dout, lse, dvec, dk, dv, BH, N, nunits, scale * kLog2e, scale,
+                       xcd_group);
   }
   {
-    const long long n8 = rows * D / 8;
-    dim3 grid((unsigned)((n8 + 255) / 256));
-    hipLaunchKernelGGL(fa_bwd_dq_kernel, grid, dim3(256), 0, stream, dqacc, dq, n8, scale);
+    using C = DqCfg<D>;
+    const int ntq = (N + C::BM - 1) / C::BM;
+    dim3 grid((unsigned)(ntq * BH));
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), grid, dim3(C::THREADS), 0, stream,
+                       q, k, v, dout, lse, dvec, dq, BH, N, ntq, scale * kLog2e, scale,
+                       xcd_group);
   }
   return hipGetLastError();
 }
 
 hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* o, const uint16_t* dout, const float* lse,
-                        uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dqacc, float* dvec,
-                        int BH, int N, int d, float scale, bool causal, hipStream_t stream) {
-  if (d == 128)
-    return causal ? launch_bwd<128, true>(q, k, v, o, dout, lse, dq, dk, dv, dqacc, dvec, BH,
-                                          N, scale, stream)
-                  : launch_bwd<128, false>(q, k, v, o, dout, lse, dq, dk, dv, dqacc, dvec, BH,
-                                           N, scale, stream);
-  return causal ? launch_bwd<64, true>(q, k, v, o, dout, lse, dq, dk, dv, dqacc, dvec, BH, N,
-                                       scale, stream)
-                : launch_bwd<64, false>(q, k, v, o, dout, lse, dq, dk, dv, dqacc, dvec, BH, N,
-                                        scale, stream);
+                        uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec, int BH, int N,
+                        int d, float scale, bool causal, hipStream_t stream) {
+#define FA_BWD_CASE(DD, CC) \
+  if (d == DD && causal == CC) \
+    return launch_bwd<DD, CC>(q, k, v, o, dout, lse, dq, dk, dv, dvec, BH, N, scale, stream);
+  FA_BWD_CASE(128, true)
+  FA_BWD_CASE(128, false)
+  FA_BWD_CASE(64, true)
+  FA_BWD_CASE(64, false)
+#undef FA_BWD_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

@@ -72,10 +72,9 @@ FA355_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float
            int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
- * Size in bytes of the workspace fa_bwd needs for this shape: an fp32
- * [B,H,N,d] dQ accumulator plus an fp32 [B,H,N] row statistic
- * D_i = sum_c dO_ic O_ic (rounded up to 256 bytes each). Returns 0 when the
- * shape is invalid.
+ * Size in bytes of the workspace fa_bwd needs for this shape: the fp32
+ * [B,H,N] row statistic D_i = sum_c dO_ic O_ic, rounded up to 256 bytes.
+ * Returns 0 when the shape is invalid.
  */
 FA355_API size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -92,8 +91,9 @@ FA355_API size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   workspace        : scratch device memory of workspace_bytes bytes, at
  *                      least fa_bwd_workspace_bytes(B,H,N,d); its contents on
  *                      entry are ignored and on return are unspecified.
- * dQ is accumulated in fp32 with atomic adds, so it may differ between runs
- * in the last bits; dK and dV are deterministic.
+ * dK and dV are accumulated over query tiles by one workgroup per key tile,
+ * dQ over key tiles by one workgroup per query tile (S and dP are computed
+ * in both), so all three gradients are deterministic.
  */
 FA355_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,

@@ -173,6 +173,18 @@ def test_bwd_small(fa, B, H, N, d, causal):
     _check_bwd(fa, B, H, N, d, causal, seed=2000 + N + d)
 
 
+def test_bwd_deterministic(fa):
+    """No cross-workgroup accumulation: two runs give bit-identical gradients."""
+    import torch
+    shape = (1, 4, 777, 128)
+    q, k, v, do = (to_gpu_bf16(fi.random_bf16(shape, 40 + i)) for i in range(4))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    g1 = fa.bwd(q, k, v, o, do, lse, causal=True)
+    g2 = fa.bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
 def test_bwd_scale_zero_and_negative(fa):
     _check_bwd(fa, 1, 2, 200, 128, True, seed=3, scale=0.0)
     _check_bwd(fa, 1, 2, 200, 64, False, seed=4, scale=-0.3)
