@@ -95,12 +95,14 @@ struct BwdCfg {
 // hits 16 distinct bank groups) and whose top bits follow row%4 (so the 4
 // rows of a transposing read fall in 4 distinct 64-byte bank quarters).
 template <int R>
+__device__ __forceinline__ int sw_xor(int row) {
+  if constexpr (R == 256) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+template <int R>
 __device__ __forceinline__ int sw_off(int row, int col) {
   const int byte = col * 2;
-  int f;
-  if constexpr (R == 256) f = ((row & 3) << 2) | ((row >> 2) & 3);
-  else f = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-  return row * R + ((((byte >> 4) ^ f)) << 4) + (byte & 15);
+  return row * R + ((((byte >> 4) ^ sw_xor<R>(row))) << 4) + (byte & 15);
 }
 
 // Global -> LDS copies (global_load_lds: lane i writes LDS bytes
@@ -122,6 +124,12 @@ __device__ __forceinline__ void lds_copy4(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(g), "s"(lds_addr) : "memory", "m0");
 }
+// Scalar-base form: the tile's base address is one SGPR pair and each lane
+// adds a 32-bit byte offset (no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void lds_copy16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
@@ -139,11 +147,7 @@ __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, const
   for (int i = 0; i < LOADS; ++i) {
     const int lrow = (w * LOADS + i) * RPL;
     const int row = lrow + lane / CPR;
-    const int pc = lane % CPR;
-    int f;
-    if constexpr (R == 256) f = ((row & 3) << 2) | ((row >> 2) & 3);
-    else f = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-    const int c = pc ^ f;
+    const int c = (lane % CPR) ^ sw_xor<R>(row);
     const uint16_t* g = src + (size_t)min(row0 + row, N - 1) * D + c * 8;
     lds_copy16(g, lds_addr(lds + lrow * R));
   }
@@ -402,6 +406,7 @@ struct DqCfg {
   static constexpr int NB = BN / 32;          // 32-key blocks per tile
   static constexpr int DB = D / 32;           // 32-wide head-dim blocks
   static constexpr int KS = D / 16;           // k-steps of S^T and dP^T
+  static_assert(KS == 2 * LOADS, "one K or V copy per k-step of the first block");
 };
 
 // dQ_i = scale * sum_j dS_ij K_j for one 128-query tile per workgroup.
@@ -481,6 +486,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int i = 0; i < DB; ++i) dqacc[i] = zero16();
 
+  // Per-lane byte offsets of this wave's K / V tile copies (lane i of copy c
+  // writes LDS bytes [16i, 16i+16) of 1 KiB block w*LOADS+c, so it fetches
+  // the chunk the swizzle puts there), for a full tile and for the ragged
+  // last tile (rows past N read row N-1).
+  uint32_t offd[C::LOADS], offr[C::LOADS];
+  {
+    constexpr int RPL = 1024 / RB, CPR = RB / 16;
+    const int kl = (N - 1) / C::BN * C::BN;
+#pragma unroll
+    for (int c = 0; c < C::LOADS; ++c) {
+      const int row = (w * C::LOADS + c) * RPL + lane / CPR;
+      const int ch = (lane % CPR) ^ sw_xor<RB>(row);
+      offd[c] = (uint32_t)(row * D + ch * 8) * 2u;
+      offr[c] = (uint32_t)(min(row, N - 1 - kl) * D + ch * 8) * 2u;
+    }
+  }
+
   // One key tile, one 32-key block at a time (one S^T / dP^T pair live):
   // S^T = K Q^T and dP^T = V dO^T (one query per lane), the exponent
   // x = S^T*scale*log2e - LSE*log2e, set to -inf for masked keys (a small
@@ -489,7 +511,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // dS^T = P^T o (dP^T - D) packed per 16-key group t (registers
   // 8*(t&1) .. +7 of the block: k-slot s of half h is key 8*(s/4) + 4h + s%4
   // of the group, the order of the transposing K reads), dQ^T += K^T dS^T.
-  auto tile = [&](const uint8_t* kt, const uint8_t* vt, int kbase, bool masked)
+  // `copy(c)` is called once after each k-step of the first block: the
+  // next tile's copies, spread over the MFMA stream.
+  auto tile = [&](const uint8_t* kt, const uint8_t* vt, int kbase, bool masked, auto&& copy)
                   __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
@@ -499,6 +523,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int o = kb * 32 * RB + rk_off[ks];
         sa = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(kt + o), qreg[ks], sa);
         pa = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(vt + o), doreg[ks], pa);
+        if (kb == 0) copy(ks);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sa[i] = fmaf(sa[i], c2, nlse2);
@@ -529,14 +554,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   for (int j = 0; j < nt; ++j) {
     const int b = j & 1;
-    if (j + 1 < nt) {
-      dma_rows<D, C::LOADS>(K + off, k_lds[b ^ 1], (j + 1) * C::BN, N, w, lane);
-      dma_rows<D, C::LOADS>(V + off, v_lds[b ^ 1], (j + 1) * C::BN, N, w, lane);
-    }
+    // Copies of K and V tile j+1 into the other buffers (copy c: K part c/2
+    // for even c, V part c/2 for odd c); on the last tile they repeat it (in
+    // bounds, unused).
+    const int kc = min(j + 1, nt - 1) * C::BN;
+    const bool full = kc + C::BN <= N;
+    auto copy = [&](int c) __attribute__((always_inline)) {
+      const int i = c >> 1;
+      uint8_t* dst = (c & 1) ? v_lds[b ^ 1] : k_lds[b ^ 1];
+      const uint16_t* src = ((c & 1) ? V : K) + off + (size_t)kc * D;
+      lds_copy16s(src, full ? offd[i] : offr[i], lds_addr(dst + (w * C::LOADS + i) * 1024));
+    };
     if (j < ntw) {
       const int kbase = j * C::BN;
       const bool masked = (CAUSAL && kbase + C::BN - 1 > qw) || kbase + C::BN > N;
-      tile(k_lds[b], v_lds[b], kbase, masked);
+      tile(k_lds[b], v_lds[b], kbase, masked, copy);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2 * C::LOADS; ++c) copy(c);
     }
     wait_vmem();
     __syncthreads();
