@@ -309,11 +309,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           sacc[qb] = mfma_32x32x16(aq, kreg[ks], sacc[qb]);
           pacc[qb] = mfma_32x32x16(ad, vreg[ks], pacc[qb]);
         }
-      // ---- P = exp2(S*scale*log2e - LSE*log2e), dS = P o (dP - D), packed to
-      // bf16 right away (k-slot order of the dV / dK B operands: 16 queries per
-      // step t, registers 8*(t&1) .. +7 of block t/2).
+      // ---- x = S*scale*log2e - LSE*log2e, set to -inf for masked entries (a
+      // small branch taken only on tiles that cross the diagonal or N; one
+      // code path keeps the exp work in the block of the dV / dK MFMAs).
       const bool masked = (CAUSAL && qbase < k0 + C::BNK - 1) || qbase + C::BMQ > N ||
                           k0 + C::BNK > N;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + 32 * qb + 8 * g4 + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[qb][4 * g4 + e] = fmaf(sacc[qb][4 * g4 + e], c2, -lse4[e] * kLog2e);
+        }
+      if (masked) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int q = qbase + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
+            sacc[qb][i] = ((CAUSAL && kk > q) || kk >= N || q >= N) ? -INFINITY : sacc[qb][i];
+          }
+      }
+      // ---- P = exp2(x), dS = P o (dP - D), packed to bf16 right away (k-slot
+      // order of the dV / dK B operands: 16 queries per step t, registers
+      // 8*(t&1) .. +7 of block t/2).
       bf16x8 pbv[C::BMQ / 16], sbv[C::BMQ / 16];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
@@ -323,17 +344,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
           for (int g2 = 0; g2 < 2; ++g2) {
             const int g4 = 2 * half + g2;
-            const int ql = 32 * qb + 8 * g4 + 4 * hi;     // first of 4 consecutive queries
-            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + ql);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + C::BMQ + ql);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + C::BMQ + 32 * qb + 8 * g4 + 4 * hi);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int i = 4 * g4 + e;
-              float p = fast_exp2(fmaf(sacc[qb][i], c2, -lse4[e] * kLog2e));
-              if (masked) {
-                const int q = qbase + ql + e;
-                if ((CAUSAL && kk > q) || kk >= N || q >= N) p = 0.f;
-              }
+              const float p = fast_exp2(sacc[qb][i]);
               pv[4 * g2 + e] = p;
               dv8[4 * g2 + e] = p * (pacc[qb][i] - d4[e]);
             }
