@@ -292,52 +292,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dma_rows<D, C::QLOADS>(dOh, o_lds[b ^ 1], qn, N, w, lane);
         if (w == 0) dma_stats(LSEh, Dh, st_lds[b ^ 1], qn, N, lane);
       }
-      // ---- S = Q K^T and dP = dO V^T (one key per lane, 32 queries per block).
-      f32x16 sacc[NQB], pacc[NQB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        sacc[qb] = zero16();
-        pacc[qb] = zero16();
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const int o = 32 * qb * RB + rq_off[ks];
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + o);
-          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(ot + o);
-          sacc[qb] = mfma_32x32x16(aq, kreg[ks], sacc[qb]);
-          pacc[qb] = mfma_32x32x16(ad, vreg[ks], pacc[qb]);
-        }
-      // ---- x = S*scale*log2e - LSE*log2e, set to -inf for masked entries (a
-      // small branch taken only on tiles that cross the diagonal or N; one
-      // code path keeps the exp work in the block of the dV / dK MFMAs).
+      // ---- Per 32-query block qb: S = Q K^T and dP = dO V^T (one key per
+      // lane), then x = S*scale*log2e - LSE*log2e (-inf where masked: a small
+      // branch taken only on tiles that cross the diagonal or N), then
+      // P = exp2(x) and dS = P o (dP - D) packed to bf16 (k-slot order of the
+      // dV / dK B operands: 16 queries per group t, registers 8*(t&1) .. +7 of
+      // block t/2). The exp / dS work of block qb sits in the same region as
+      // the S / dP MFMAs of block qb+1, and that of the last block beside the
+      // first dV / dK MFMAs, so one wave overlaps MFMA and VALU work.
       const bool masked = (CAUSAL && qbase < k0 + C::BNK - 1) || qbase + C::BMQ > N ||
                           k0 + C::BNK > N;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + 32 * qb + 8 * g4 + 4 * hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sacc[qb][4 * g4 + e] = fmaf(sacc[qb][4 * g4 + e], c2, -lse4[e] * kLog2e);
-        }
-      if (masked) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int q = qbase + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
-            sacc[qb][i] = ((CAUSAL && kk > q) || kk >= N || q >= N) ? -INFINITY : sacc[qb][i];
-          }
-      }
-      // ---- P = exp2(x), dS = P o (dP - D), packed to bf16 right away (k-slot
-      // order of the dV / dK B operands: 16 queries per step t, registers
-      // 8*(t&1) .. +7 of block t/2).
+      constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+      f32x16 sacc[NQB], pacc[NQB];
       bf16x8 pbv[C::BMQ / 16], sbv[C::BMQ / 16];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+      auto exp_pack = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           float pv[8], dv8[8];
@@ -357,6 +325,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           pbv[t] = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
           sbv[t] = pack_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
         }
+      };
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        sacc[qb] = zero16();
+        pacc[qb] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int o = 32 * qb * RB + rq_off[ks];
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + o);
+          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(ot + o);
+          sacc[qb] = mfma_32x32x16(aq, kreg[ks], sacc[qb]);
+          pacc[qb] = mfma_32x32x16(ad, vreg[ks], pacc[qb]);
+        }
+        if (qb > 0) {
+          exp_pack(qb - 1);
+          // Keep that work in this region (its results are only used by the
+          // dV / dK MFMAs, into whose block the compiler would sink it).
+#pragma unroll
+          for (int t = 2 * (qb - 1); t < 2 * qb; ++t) asm volatile("" : "+v"(pbv[t]), "+v"(sbv[t]));
+          // S / dP MFMAs of this block, each with one operand read and the
+          // exp / dS / packing work of the previous block.
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
+#pragma unroll
+          for (int i = 0; i < 2 * KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kValu, 5, 0);
+          }
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + 32 * qb + 8 * g4 + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[qb][4 * g4 + e] = fmaf(sacc[qb][4 * g4 + e], c2, -lse4[e] * kLog2e);
+        }
+        if (masked) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int q = qbase + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
+            sacc[qb][i] = ((CAUSAL && kk > q) || kk >= N || q >= N) ? -INFINITY : sacc[qb][i];
+          }
+        }
+      }
+      exp_pack(NQB - 1);
       // ---- dV^T += dO^T P and dK^T += Q^T dS (k-slots = queries).
 #pragma unroll
       for (int t = 0; t < C::BMQ / 16; ++t) {
@@ -367,20 +380,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
       }
       {
-        constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
-        // S / dP MFMAs each with one operand read; the dV / dK MFMAs each with
-        // two transposing reads and the exp / dS / packing work.
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * KS * NQB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
-        }
+        // dV / dK MFMAs, each with two transposing reads issued 8 MFMAs
+        // ahead (the LDS latency is not hidden by a second wave here); the
+        // first ones also carry the exp / dS / packing work of the last block.
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 16, 0);
 #pragma unroll
         for (int i = 0; i < 2 * (C::BMQ / 16) * DB; ++i) {
           __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
           __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(kValu, 5, 0);
         }
       }
       wait_vmem();
