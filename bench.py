@@ -41,6 +41,9 @@ def parse():
                    help="approximate CPU time budget of the oracle sample")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--unfused", action="store_true",
+                   help="also time the unfused comparator (S and P in device memory) on the "
+                        "same forward inputs and report the fused forward's speedup over it")
     return p.parse_args()
 
 
@@ -189,6 +192,37 @@ def main():
                 "traffic": dom["traffic"],
                 "kernel": dom["launch"], "avg_launch_ms": round(dom["avg_ms"], 4)}
 
+    unfused = None
+    if args.unfused:
+        ws_u = torch.empty(fa.fa_unfused_workspace_bytes(w.B, w.H, w.N, w.d), device=dev,
+                           dtype=torch.uint8)
+        o_u = torch.empty_like(q)
+        lse_u = torch.empty_like(lse)
+
+        def ufwd():
+            fa.unfused_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o_u, lse=lse_u,
+                           workspace=ws_u)
+
+        for _ in range(3):
+            ufwd()
+        torch.cuda.synchronize()
+        n_u = max(3, min(args.steps, 30))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_u):
+            ufwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        u_ms = e0.elapsed_time(e1) / n_u
+        unfused = {"avg_ms": round(u_ms, 4), "calls": n_u,
+                   "fwd_tflops_equiv": round(w.fwd_flops() / (u_ms * 1e-3) / 1e12, 2),
+                   "fused_fwd_speedup": round(u_ms / f_avg, 2),
+                   "workspace_GB": round(ws_u.numel() / 1e9, 3),
+                   "note": "S = scale*QK^T (fp32) and P (bf16) round-trip device memory; "
+                           "library GEMMs for QK^T and PV, hand-written row softmax; the "
+                           "full N x N is computed also when causal"}
+        del ws_u
+
     if args.copy_calib_mib > 0:
         src = torch.empty(args.copy_calib_mib * 2 ** 20, device=dev, dtype=torch.uint8)
         dst = torch.empty_like(src)
@@ -222,6 +256,8 @@ def main():
         rec["bwd"] = {"avg_ms": round(b_avg, 4), "min_ms": round(min(bwd_ms), 4),
                       "tflops": round(bwd_tf, 2),
                       "hbm_alg_GBs": round(bwd_bytes(w) / (b_avg * 1e-3) / 1e9, 1)}
+    if unfused is not None:
+        rec["unfused"] = unfused
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -15,7 +15,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa355.so")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_unfused.hip", "fa_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -43,7 +43,8 @@ def build(extra: list[str] | None = None) -> str:
         with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
             list(ex.map(lambda a: _compile(a[0], a[1], extra), zip(SOURCES, objs)))
         out_tmp = LIB + ".tmp"
-        cmd = [HIPCC, *COMMON, "-shared", *objs, "-o", out_tmp]
+        # rocBLAS serves the two plain GEMMs of the unfused comparator.
+        cmd = [HIPCC, *COMMON, "-shared", *objs, "-o", out_tmp, "-L/opt/rocm/lib", "-lrocblas"]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -16,6 +16,9 @@ hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* o, const uint16_t* dout, const float* lse,
                         uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec, int BH, int N,
                         int d, float scale, bool causal, hipStream_t stream);
+hipError_t unfused_fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                uint16_t* o, float* lse, float* ws, int BH, int N, int d,
+                                float scale, bool causal, hipStream_t stream, bool* blas_failed);
 }  // namespace fa
 
 namespace {
@@ -82,6 +85,33 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_unfused_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  return round256((size_t)B * H * N * (size_t)N * sizeof(float));
+}
+
+int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != FA_OK) return rc;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const size_t need = fa_unfused_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, lse, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  bool blas_failed = false;
+  hipError_t e = fa::unfused_fwd_dispatch(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+      static_cast<float*>(workspace), B * H, N, d, scale, causal != 0,
+      static_cast<hipStream_t>(stream), &blas_failed);
+  if (blas_failed) return FA_ERR_BLAS;
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_strerror(int code) {
   switch (code) {
     case FA_OK: return "success";
@@ -92,6 +122,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
     case FA_ERR_WORKSPACE: return "backward workspace is NULL or too small";
     case FA_ERR_HIP: return "the HIP runtime reported a launch error";
+    case FA_ERR_BLAS: return "rocBLAS reported an error (unfused comparator only)";
     default: return "unknown fa355 error code";
   }
 }

@@ -6,8 +6,9 @@ the C ABI, and every step of the computation runs in the library's kernels.
 PyTorch only supplies device memory and the stream. There is no fallback: if
 the library cannot be loaded, every call raises.
 
-The functions ``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes`` and
-``fa_strerror`` are the raw C entry points (ctypes). ``fwd`` / ``bwd`` are
+The functions ``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes``,
+``fa_unfused_fwd``, ``fa_unfused_workspace_bytes`` and ``fa_strerror`` are the
+raw C entry points (ctypes). ``fwd`` / ``bwd`` / ``unfused_fwd`` are
 tensor-level wrappers with the same semantics.
 """
 from __future__ import annotations
@@ -19,7 +20,7 @@ import os
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_SCALE, FA_ERR_ALIGN, \
-    FA_ERR_WORKSPACE, FA_ERR_HIP = range(8)
+    FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_BLAS = range(9)
 
 
 class FAError(RuntimeError):
@@ -54,6 +55,10 @@ def _load():
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_unfused_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_unfused_workspace_bytes.restype = sz
+    lib.fa_unfused_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    lib.fa_unfused_fwd.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -78,6 +83,16 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, 
 
 def fa_bwd_workspace_bytes(B, H, N, d) -> int:
     return _load().fa_bwd_workspace_bytes(B, H, N, d)
+
+
+def fa_unfused_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale, causal,
+                   stream) -> int:
+    return _load().fa_unfused_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d,
+                                  scale, int(causal), stream)
+
+
+def fa_unfused_workspace_bytes(B, H, N, d) -> int:
+    return _load().fa_unfused_workspace_bytes(B, H, N, d)
 
 
 def fa_strerror(code: int) -> str:
@@ -166,3 +181,35 @@ def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None
     if rc != FA_OK:
         raise FAError(rc, "fa_bwd")
     return dq, dk, dv
+
+
+def unfused_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None,
+                lse=None, workspace=None, stream=None):
+    """The same O, LSE as ``fwd`` by the unfused three-step method (S and P in
+    device memory): the measured comparator of the fused pass."""
+    import torch
+    _check(q, "q", dtype=torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    _check(k, "k", q.shape, torch.bfloat16)
+    _check(v, "v", q.shape, torch.bfloat16)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    _check(out, "out", q.shape, torch.bfloat16)
+    _check(lse, "lse", (B, H, N), torch.float32)
+    need = fa_unfused_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _check(workspace, "workspace")
+    rc = fa_unfused_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr(), workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), B, H, N, d, float(scale),
+                        causal, _stream_ptr(q.device, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_unfused_fwd")
+    return out, lse

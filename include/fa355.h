@@ -29,8 +29,11 @@
  *     enqueue work and return; results are visible after the stream is
  *     synchronised. Kernel faults surface at that synchronisation.
  *   - Ownership: the caller allocates and frees every buffer, including the
- *     backward workspace. The library keeps no state between calls, allocates
- *     no memory and is safe to call from several host threads.
+ *     workspaces. fa_fwd and fa_bwd keep no state between calls, allocate no
+ *     memory and are safe to call from several host threads. The unfused
+ *     comparator (fa_unfused_fwd) creates one rocBLAS handle per device on
+ *     its first call there (rocBLAS allocates its own scratch memory then)
+ *     and keeps it until the process ends.
  *   - Errors: 0 (FA_OK) on success, else one of the FA_ERR_* codes below.
  *     Arguments are validated before any HIP call, so an invalid call launches
  *     nothing and touches no memory. No C++ exception crosses this ABI.
@@ -58,7 +61,8 @@ enum {
   FA_ERR_SCALE = 4,     /* scale is NaN or infinite                          */
   FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                  */
   FA_ERR_WORKSPACE = 6, /* backward workspace NULL or smaller than required  */
-  FA_ERR_HIP = 7        /* the HIP runtime reported a launch error           */
+  FA_ERR_HIP = 7,       /* the HIP runtime reported a launch error           */
+  FA_ERR_BLAS = 8       /* rocBLAS reported an error (fa_unfused_fwd only)   */
 };
 
 /*
@@ -97,6 +101,28 @@ FA355_API size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  */
 FA355_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+           float scale, int causal, void* stream);
+
+/*
+ * Unfused ("standard") attention: the same O and LSE as fa_fwd, computed by
+ * the three-step decomposition that the fused pass avoids, kept as a
+ * measured comparator. Method: the interview answer's "standard attention"
+ * steps and "FlashAttention and Triton" (chapter 19), section 19.2:
+ *   1. S = scale * Q K^T is written to memory (fp32, library GEMM);
+ *   2. a row-wise softmax pass (section 19.11: one workgroup per row, row
+ *      max, exp, row sum) reads S, applies the causal mask and writes P
+ *      (bf16) and the LSE;
+ *   3. O = P V (library GEMM, fp32 accumulate, bf16 out).
+ *   q, k, v, o, lse  : as for fa_fwd
+ *   workspace        : device memory of workspace_bytes bytes, at least
+ *                      fa_unfused_workspace_bytes(B,H,N,d): holds S as fp32
+ *                      [B,H,N,N], then P as bf16 over the first half of each
+ *                      S row; contents on return are unspecified.
+ * Returns FA_ERR_BLAS when rocBLAS fails.
+ */
+FA355_API size_t fa_unfused_workspace_bytes(int B, int H, int N, int d);
+FA355_API int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
            float scale, int causal, void* stream);
 

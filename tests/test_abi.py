@@ -32,7 +32,8 @@ def fa():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_strerror"]
+    assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_strerror",
+                           "fa_unfused_fwd", "fa_unfused_workspace_bytes"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -45,7 +46,7 @@ def test_every_declared_symbol_is_exported():
 def test_codes_match_binding(fa):
     codes = _codes()
     assert codes["FA_OK"] == fa.FA_OK == 0
-    for n in ("NULL", "SHAPE", "HEADDIM", "SCALE", "ALIGN", "WORKSPACE", "HIP"):
+    for n in ("NULL", "SHAPE", "HEADDIM", "SCALE", "ALIGN", "WORKSPACE", "HIP", "BLAS"):
         assert codes["FA_ERR_" + n] == getattr(fa, "FA_ERR_" + n)
         assert fa.fa_strerror(codes["FA_ERR_" + n]) not in ("", "unknown fa355 error code")
     assert fa.fa_strerror(99) == "unknown fa355 error code"
@@ -147,3 +148,37 @@ def test_single_hip_runtime_mapped():
                          text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+# ---------------------------------------------------------------- unfused comparator
+def _unf(fa, ws=GOOD, ws_bytes=None, B=1, H=1, N=16, d=64, scale=0.125, **ptrs):
+    p = dict(q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_unfused_workspace_bytes(1, 1, 16, 64)
+    return fa.fa_unfused_fwd(p["q"], p["k"], p["v"], p["o"], p["lse"], ws, ws_bytes, B, H, N,
+                             d, scale, 1, None)
+
+
+def test_unfused_workspace_bytes(fa):
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert fa.fa_unfused_workspace_bytes(2, 16, 2048, 128) == r256(2 * 16 * 2048 * 2048 * 4)
+    assert fa.fa_unfused_workspace_bytes(1, 1, 1, 64) == 256
+    assert fa.fa_unfused_workspace_bytes(1, 0, 8, 64) == 0
+    assert fa.fa_unfused_workspace_bytes(1, 1, 8, 96) == 0
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_unfused_null_and_align(fa, which):
+    assert _unf(fa, **{which: None}) == fa.FA_ERR_NULL
+    assert _unf(fa, **{which: GOOD + 4}) == fa.FA_ERR_ALIGN
+
+
+def test_unfused_validation(fa):
+    need = fa.fa_unfused_workspace_bytes(1, 1, 16, 64)
+    assert _unf(fa, ws=None) == fa.FA_ERR_WORKSPACE
+    assert _unf(fa, ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    assert _unf(fa, ws=GOOD + 8) == fa.FA_ERR_ALIGN
+    assert _unf(fa, N=0) == fa.FA_ERR_SHAPE
+    assert _unf(fa, d=32) == fa.FA_ERR_HEADDIM
+    assert _unf(fa, scale=math.nan) == fa.FA_ERR_SCALE
