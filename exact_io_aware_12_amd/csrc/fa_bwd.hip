@@ -77,16 +77,19 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct BwdCfg {
-  static constexpr int WAVES = 4;
-  static constexpr int THREADS = 256;
-  static constexpr int BNK = 128;          // keys per workgroup (32 per wave)
-  static constexpr int BMQ = 64;           // queries per inner tile
-  static constexpr int RB = D * 2;         // bytes per Q / dO row in LDS
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BNK = 128;          // keys per workgroup: 4 key blocks of 32
+  static constexpr int BMQ = 64;           // queries per step: 2 halves of 32
+  static constexpr int RB = D * 2;         // bytes per Q / dO / V row in LDS
   static constexpr int QTILE = BMQ * RB;   // 16 KiB (d=128)
+  static constexpr int VTILE = BNK * RB;   // 32 KiB (d=128): one K or V key tile
   static constexpr int QLOADS = QTILE / 1024 / WAVES;   // 1 KiB copies per wave
+  static constexpr int VLOADS = VTILE / 1024 / WAVES;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int NQB = BMQ / 32;     // 32-query blocks per tile
+  // The pair's partial dK (then dV) sums go through the Q / dO buffers.
+  static_assert(4 * 16 * DB * 64 * 4 <= 4 * QTILE, "partial sums fit the Q/dO buffers");
 };
 
 // Swizzled byte offset of 2-byte element (row, col) in a tile with R-byte
@@ -176,22 +179,29 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* base, int o0, int o1
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_dkdv_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dvec,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     int BH, int N, int nunits, float c2, float scale, int xcd_group) {
   using C = BwdCfg<D>;
-  constexpr int KS = C::KS, DB = C::DB, NQB = C::NQB, RB = C::RB;
-  __shared__ __attribute__((aligned(1024))) uint8_t q_lds[2][C::QTILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t o_lds[2][C::QTILE];   // dO tiles
-  __shared__ __attribute__((aligned(256))) float st_lds[2][2 * C::BMQ];   // LSE, D
+  constexpr int KS = C::KS, DB = C::DB, RB = C::RB;
+  // Q tiles (buffers 0, 1) then dO tiles (buffers 2, 3); at the end of a key
+  // tile the same bytes carry the partial dK / dV sums.
+  __shared__ __attribute__((aligned(1024))) uint8_t qo_lds[4 * C::QTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[C::VTILE];      // this key tile's K
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[C::VTILE];      // and V
+  __shared__ __attribute__((aligned(256))) float st_lds[2][2 * C::BMQ];    // LSE, D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
+  // Wave w: keys 32*kb .. +31 of the key tile, queries 32*qh .. +31 of each
+  // query tile. The two waves of a key block (qh = 0, 1) share a SIMD with
+  // waves of other key blocks, and their partial dK / dV are summed at the end.
+  const int kb = w & 3, qh = w >> 2;
 
   // Workgroup -> (head, work unit). Causal: unit u covers the key tiles u and
   // nkt-1-u: first key tile u with the query tiles in descending order, then
@@ -226,21 +236,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // (plus 32*block) of a row-major tile.
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
   // Per-lane LDS offsets. The swizzles only look at bits 0-3 of the row, so
   // whole 16-row (and 32-row) steps are plain immediate offsets: one register
   // per (half, 32-column block) for transposing reads, one per k-step for
-  // the row-major operand reads.
-  int tq_off[2][DB];            // Q / dO tiles, transposing reads
+  // the row-major operand reads (Q, dO, K and V rows alike).
+  int tq_off[2][DB];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int db = 0; db < DB; ++db) tq_off[h][db] = sw_off<RB>(tr_row + 8 * h, 32 * db + tr_col);
-  int rq_off[KS];               // Q / dO tiles, row-major reads of row l32
+  int rq_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) rq_off[ks] = sw_off<RB>(l32, 16 * ks + 8 * hi);
 
-  bf16x8 kreg[KS], vreg[KS];          // this lane's key row of K and V (B operands)
   f32x16 dkacc[DB], dvacc[DB];
   int k0 = 0, kk = 0;                 // first key of the tile, this lane's key
 
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int part = 0; part < nparts; ++part) {
     const int kt = part == 0 ? unit : nkt_ - 1 - unit;
     k0 = kt * C::BNK;
-    kk = k0 + 32 * w + l32;
+    kk = k0 + 32 * kb + l32;
     // Query tiles it_lo .. nqt-1 (causal: from the one holding key k0), in
     // descending order in the first part of a causal unit.
     const bool rev = CAUSAL && part == 0;
@@ -259,120 +267,89 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       return rev ? nqt - 1 - step : it_lo + step;
     };
 
-    // Copies: the first query tile.
-    dma_rows<D, C::QLOADS>(Qh, q_lds[0], tile_at(0) * C::BMQ, N, w, lane);
-    dma_rows<D, C::QLOADS>(dOh, o_lds[0], tile_at(0) * C::BMQ, N, w, lane);
+    // Copies: this key tile's K and V, the first query tile.
+    dma_rows<D, C::VLOADS>(K + off, k_lds, k0, N, w, lane);
+    dma_rows<D, C::VLOADS>(V + off, v_lds, k0, N, w, lane);
+    dma_rows<D, C::QLOADS>(Qh, qo_lds, tile_at(0) * C::BMQ, N, w, lane);
+    dma_rows<D, C::QLOADS>(dOh, qo_lds + 2 * C::QTILE, tile_at(0) * C::BMQ, N, w, lane);
     if (w == 0) dma_stats(LSEh, Dh, st_lds[0], tile_at(0) * C::BMQ, N, lane);
-    {
-      const size_t o = (size_t)min(kk, N - 1) * D + hi * 8;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(K + off + o + ks * 16));
-        vreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(V + off + o + ks * 16));
-      }
-    }
-    wait_vmem();
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
       dkacc[i] = zero16();
       dvacc[i] = zero16();
     }
+    wait_vmem();
+    __syncthreads();
 
+    const uint8_t* krows = k_lds + 32 * kb * RB;   // this wave's 32 K rows
+    const uint8_t* vrows = v_lds + 32 * kb * RB;   // and V rows
     for (int step = 0; step < nsteps; ++step) {
-      // Buffers of this query tile (b) and of the next one (b ^ 1).
+      // Buffers of this query tile (b) and of the next one (b ^ 1); this
+      // wave's 32 queries start 32*qh rows into the tile.
       const int b = step & 1;
-      const uint8_t* qt = q_lds[b];
-      const uint8_t* ot = o_lds[b];
-      const float* st = st_lds[b];
+      const uint8_t* qt = qo_lds + b * C::QTILE + 32 * qh * RB;
+      const uint8_t* ot = qo_lds + (2 + b) * C::QTILE + 32 * qh * RB;
+      const float* st = st_lds[b] + 32 * qh;
       const int qbase = tile_at(step) * C::BMQ;
+      const int qw = qbase + 32 * qh;            // first query of this wave
       if (step + 1 < nsteps) {
         const int qn = tile_at(step + 1) * C::BMQ;
-        dma_rows<D, C::QLOADS>(Qh, q_lds[b ^ 1], qn, N, w, lane);
-        dma_rows<D, C::QLOADS>(dOh, o_lds[b ^ 1], qn, N, w, lane);
+        dma_rows<D, C::QLOADS>(Qh, qo_lds + (b ^ 1) * C::QTILE, qn, N, w, lane);
+        dma_rows<D, C::QLOADS>(dOh, qo_lds + (2 + (b ^ 1)) * C::QTILE, qn, N, w, lane);
         if (w == 0) dma_stats(LSEh, Dh, st_lds[b ^ 1], qn, N, lane);
       }
-      // ---- Per 32-query block qb: S = Q K^T and dP = dO V^T (one key per
-      // lane), then x = S*scale*log2e - LSE*log2e (-inf where masked: a small
-      // branch taken only on tiles that cross the diagonal or N), then
-      // P = exp2(x) and dS = P o (dP - D) packed to bf16 (k-slot order of the
-      // dV / dK B operands: 16 queries per group t, registers 8*(t&1) .. +7 of
-      // block t/2). The exp / dS work of block qb sits in the same region as
-      // the S / dP MFMAs of block qb+1, and that of the last block beside the
-      // first dV / dK MFMAs, so one wave overlaps MFMA and VALU work.
-      const bool masked = (CAUSAL && qbase < k0 + C::BNK - 1) || qbase + C::BMQ > N ||
-                          k0 + C::BNK > N;
-      constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
-      f32x16 sacc[NQB], pacc[NQB];
-      bf16x8 pbv[C::BMQ / 16], sbv[C::BMQ / 16];
-      auto exp_pack = [&](int qb) __attribute__((always_inline)) {
+      // ---- S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+      // (one key per lane: K and V rows from LDS as B operands).
+      f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float pv[8], dv8[8];
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + rq_off[ks]);
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(ot + rq_off[ks]);
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(krows + rq_off[ks]);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vrows + rq_off[ks]);
+        sacc = mfma_32x32x16(aq, bk, sacc);
+        pacc = mfma_32x32x16(ad, bv, pacc);
+      }
+      // ---- x = S*scale*log2e - LSE*log2e, -inf where masked (a small branch
+      // taken only on tiles that cross the diagonal or N), P = exp2(x),
+      // dS = P o (dP - D), packed to bf16 per 16-query group t (registers
+      // 8t .. 8t+7: the k-slot order of the dV / dK B operands).
+      const bool masked = (CAUSAL && qw < kk - l32 + 31) || qw + 32 > N || k0 + C::BNK > N;
 #pragma unroll
-          for (int g2 = 0; g2 < 2; ++g2) {
-            const int g4 = 2 * half + g2;
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + C::BMQ + 32 * qb + 8 * g4 + 4 * hi);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + 8 * g4 + 4 * hi);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * g4 + e;
-              const float p = fast_exp2(sacc[qb][i]);
-              pv[4 * g2 + e] = p;
-              dv8[4 * g2 + e] = p * (pacc[qb][i] - d4[e]);
-            }
-          }
-          const int t = 2 * qb + half;
-          pbv[t] = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-          sbv[t] = pack_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
-        }
-      };
+        for (int e = 0; e < 4; ++e)
+          sacc[4 * g4 + e] = fmaf(sacc[4 * g4 + e], c2, -lse4[e] * kLog2e);
+      }
+      if (masked) {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        sacc[qb] = zero16();
-        pacc[qb] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int o = 32 * qb * RB + rq_off[ks];
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + o);
-          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(ot + o);
-          sacc[qb] = mfma_32x32x16(aq, kreg[ks], sacc[qb]);
-          pacc[qb] = mfma_32x32x16(ad, vreg[ks], pacc[qb]);
-        }
-        if (qb > 0) {
-          exp_pack(qb - 1);
-          // Keep that work in this region (its results are only used by the
-          // dV / dK MFMAs, into whose block the compiler would sink it).
-#pragma unroll
-          for (int t = 2 * (qb - 1); t < 2 * qb; ++t) asm volatile("" : "+v"(pbv[t]), "+v"(sbv[t]));
-          // S / dP MFMAs of this block, each with one operand read and the
-          // exp / dS / packing work of the previous block.
-          __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
-#pragma unroll
-          for (int i = 0; i < 2 * KS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kValu, 5, 0);
-          }
-        }
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + 32 * qb + 8 * g4 + 4 * hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sacc[qb][4 * g4 + e] = fmaf(sacc[qb][4 * g4 + e], c2, -lse4[e] * kLog2e);
-        }
-        if (masked) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int q = qbase + 32 * qb + 8 * (i >> 2) + 4 * hi + (i & 3);
-            sacc[qb][i] = ((CAUSAL && kk > q) || kk >= N || q >= N) ? -INFINITY : sacc[qb][i];
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int q = qw + 8 * (i >> 2) + 4 * hi + (i & 3);
+          sacc[i] = ((CAUSAL && kk > q) || kk >= N || q >= N) ? -INFINITY : sacc[i];
         }
       }
-      exp_pack(NQB - 1);
-      // ---- dV^T += dO^T P and dK^T += Q^T dS (k-slots = queries).
+      bf16x8 pbv[2], sbv[2];
 #pragma unroll
-      for (int t = 0; t < C::BMQ / 16; ++t) {
+      for (int t = 0; t < 2; ++t) {
+        float pv[8], dv8[8];
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g4 = 2 * t + g2;
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + C::BMQ + 8 * g4 + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = fast_exp2(sacc[4 * g4 + e]);
+            pv[4 * g2 + e] = p;
+            dv8[4 * g2 + e] = p * (pacc[4 * g4 + e] - d4[e]);
+          }
+        }
+        pbv[t] = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        sbv[t] = pack_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
+      }
+      // ---- dV^T += dO^T P and dK^T += Q^T dS (k-slots = this wave's queries).
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           dvacc[db] = mfma_32x32x16(tr_operand(ot + 16 * t * RB, tq_off[0][db], tq_off[1][db]), pbv[t], dvacc[db]);
@@ -380,12 +357,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
       }
       {
-        // dV / dK MFMAs, each with two transposing reads issued 8 MFMAs
-        // ahead (the LDS latency is not hidden by a second wave here); the
-        // first ones also carry the exp / dS / packing work of the last block.
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 16, 0);
+        constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+        // S / dP MFMAs with their operand reads, then the dV / dK MFMAs with
+        // two transposing reads each and the exp / dS / packing work.
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * (C::BMQ / 16) * DB; ++i) {
+        for (int i = 0; i < 2 * KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4 * DB; ++i) {
           __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
           __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
           __builtin_amdgcn_sched_group_barrier(kValu, 5, 0);
@@ -395,24 +377,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __syncthreads();
     }
 
-    // ---- dK = scale * dK^T, dV = dV^T (one key per lane; 4 consecutive d).
-    if (kk < N) {
-      uint16_t* dkrow = dK + off + (size_t)kk * D;
-      uint16_t* dvrow = dV + off + (size_t)kk * D;
+    // ---- Sum the pair's partial dK^T, dV^T through LDS (lane-contiguous
+    // fp32, conflict-free) and store dK = scale * dK^T, dV = dV^T (one key
+    // per lane; 4 consecutive d per store). Every Q / dO read of this key
+    // tile finished before the last barrier.
+    float* red = reinterpret_cast<float*>(qo_lds) + kb * (DB * 16 * 64) + lane;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int which = 0; which < 2; ++which) {
+      f32x16 (&acc)[DB] = which == 0 ? dkacc : dvacc;
+      if (qh == 1) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = db * 32 + 8 * g4 + 4 * hi;
-          const f32x16& a = dkacc[db];
-          const f32x16& b = dvacc[db];
-          u32x2 pk = {pack_bf16x2(a[4 * g4] * scale, a[4 * g4 + 1] * scale),
-                      pack_bf16x2(a[4 * g4 + 2] * scale, a[4 * g4 + 3] * scale)};
-          u32x2 pv = {pack_bf16x2(b[4 * g4], b[4 * g4 + 1]),
-                      pack_bf16x2(b[4 * g4 + 2], b[4 * g4 + 3])};
-          *reinterpret_cast<u32x2*>(dkrow + d0) = pk;
-          *reinterpret_cast<u32x2*>(dvrow + d0) = pv;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) red[(db * 16 + i) * 64] = acc[db][i];
+      }
+      __syncthreads();
+      if (qh == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] += red[(db * 16 + i) * 64];
+        if (kk < N) {
+          uint16_t* row = (which == 0 ? dK : dV) + off + (size_t)kk * D;
+          const float sc = which == 0 ? scale : 1.f;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int d0 = db * 32 + 8 * g4 + 4 * hi;
+              u32x2 pk = {pack_bf16x2(acc[db][4 * g4] * sc, acc[db][4 * g4 + 1] * sc),
+                          pack_bf16x2(acc[db][4 * g4 + 2] * sc, acc[db][4 * g4 + 3] * sc)};
+              *reinterpret_cast<u32x2*>(row + d0) = pk;
+            }
         }
+      }
+      __syncthreads();   // the buffers are read (then refilled) again after this
     }
   }
 }
