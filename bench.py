@@ -180,7 +180,7 @@ def main():
     fwd_tf = w.fwd_flops() / (f_avg * 1e-3) / 1e12
     bwd_tf = (w.bwd_flops() / (b_avg * 1e-3) / 1e12) if w.backward else None
     if w.backward and b_avg > f_avg:
-        dom = {"launch": "fa_bwd (kernels fa_bwd_pre, fa_bwd_dkdv, fa_bwd_dq back to back)",
+        dom = {"launch": "fa_bwd (kernels fa_bwd_dq, fa_bwd_dkdv back to back)",
                "achieved": bwd_tf, "avg_ms": b_avg,
                "traffic": recorded_traffic(args.workload, "fa_bwd")}
     else:

@@ -8,14 +8,15 @@
 // dO_i . O_i); taken per tile it would not be the gradient, so it is computed
 // once per row before the tile loops.
 //
-// Three kernels on the caller's stream:
-//   1. fa_bwd_pre:   D_i = dO_i . O_i (fp32).
-//   2. fa_bwd_dkdv:  dK and dV. One workgroup per key tile pair (4 wave64s x
-//      32 keys, one wave per SIMD); the loop runs over 64-query tiles (outer
-//      loop over K/V, inner over Q, so dK and dV stay in registers).
-//   3. fa_bwd_dq:    dQ. One workgroup per 128-query tile (4 wave64s x 32
-//      queries, two workgroups per CU); the loop runs over 64-key tiles and
-//      recomputes S and dP (inner loop over K/V, so dQ stays in registers).
+// Two kernels on the caller's stream:
+//   1. fa_bwd_dq:    D_i = dO_i . O_i (written out) and dQ. One workgroup per
+//      128-query tile (4 wave64s x 32 queries, two workgroups per CU); the
+//      loop runs over 64-key tiles and recomputes S and dP (inner loop over
+//      K/V, so dQ stays in registers).
+//   2. fa_bwd_dkdv:  dK and dV. One workgroup per key tile pair (8 wave64s,
+//      two per SIMD: 4 key blocks of 32 x 2 query halves); the loop runs over
+//      64-query tiles (outer loop over K/V, inner over Q, so dK and dV stay
+//      in registers).
 // Splitting dQ from dK/dV costs two extra matmuls per tile pair (S and dP are
 // computed in both kernels: 7 instead of 5), and buys the removal of every
 // cross-workgroup accumulation: on this multi-XCD device, device-scope fp32
@@ -24,13 +25,14 @@
 //
 // gfx950 mapping (32x32x16 bf16 MFMAs, fp32 accumulate):
 //   * dK/dV kernel: S = Q K^T and dP = dO V^T are computed with one key per
-//     lane (the B operands K and V of this wave's 32 keys live in registers),
-//     so P and dS sit in registers in exactly the layout the B operand of
-//     dV^T += dO^T P and dK^T += Q^T dS needs (k-slots are queries). Q and dO
-//     tiles go from HBM/L2 straight into LDS (global_load_lds_dwordx4,
-//     double-buffered) in one XOR swizzle that serves both the row-major
-//     operand reads of S and dP (ds_read_b128) and the transposing reads that
-//     give Q^T and dO^T (ds_read_b64_tr_b16) without bank conflicts.
+//     lane (the B operands are this wave's 32 rows of the key tile's K and V,
+//     staged in LDS once per key tile), so P and dS sit in registers in
+//     exactly the layout the B operand of dV^T += dO^T P and
+//     dK^T += Q^T dS needs (k-slots are queries). Q and dO tiles go from
+//     HBM/L2 straight into LDS (global_load_lds_dwordx4, double-buffered) in
+//     one XOR swizzle that serves both the row-major operand reads of S and
+//     dP (ds_read_b128) and the transposing reads that give Q^T and dO^T
+//     (ds_read_b64_tr_b16) without bank conflicts.
 //   * dQ kernel: the transposed form of the forward pass, one query per lane:
 //     S^T = K Q^T and dP^T = V dO^T (Q and dO rows in registers as B
 //     operands, K and V rows from LDS), P^T and dS^T element-wise with the
@@ -45,32 +47,7 @@
 
 namespace fa {
 
-// ----------------------------------------------------------------- kernel 1
-template <int D>
-__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(
-    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-    float* __restrict__ Dvec, long long rows) {
-  constexpr int TPR = D / 8;            // threads per row, 8 elements each
-  constexpr int RPB = 256 / TPR;        // rows per block
-  const int tid = threadIdx.x;
-  const long long row = (long long)blockIdx.x * RPB + tid / TPR;
-  const int c = tid % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 a = ld_global_16B(O + row * D + c * 8);
-    const u32x4 b = ld_global_16B(dO + row * D + c * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc += __uint_as_float(a[e] << 16) * __uint_as_float(b[e] << 16);
-      acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(b[e] & 0xffff0000u);
-    }
-  }
-#pragma unroll
-  for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
-  if (row < rows && c == 0) Dvec[row] = acc;
-}
-
-// ----------------------------------------------------------------- kernel 2
+// ----------------------------------------------------------------- dK, dV
 #define LDS_AS __attribute__((address_space(3)))
 #define GLB_AS __attribute__((address_space(1)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -416,7 +393,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// ----------------------------------------------------------------- kernel 3
+// ----------------------------------------------------------------- dQ (and D)
 template <int D>
 struct DqCfg {
   static constexpr int BM = 128;              // queries per workgroup (32 per wave)
@@ -436,7 +413,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    const uint16_t* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ Dvec,
     uint16_t* __restrict__ dQ, int BH, int N, int ntq, float c2, float scale, int xcd_group) {
   using C = DqCfg<D>;
   constexpr int KS = C::KS, DB = C::DB, NB = C::NB, RB = C::RB;
@@ -477,18 +454,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   dma_rows<D, C::LOADS>(V + off, v_lds[0], 0, N, w, lane);
 
   // This lane's Q and dO rows as B operands (k-slots = head dim), and its
-  // row statistics: LSE in log2 units and D.
+  // row statistics: LSE in log2 units and D = dO . O (B1), summed over the
+  // lane's half of the row and exchanged with the other half. D is also
+  // written out for the dK / dV kernel, which runs after this one.
   bf16x8 qreg[KS], doreg[KS];
+  float dpart = 0.f;
   {
     const size_t o = off + (size_t)qc * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(Q + o + ks * 16));
       doreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(dO + o + ks * 16));
+      const u32x4 ov = ld_global_16B(O + o + ks * 16);
+      const u32x4 dv = __builtin_bit_cast(u32x4, doreg[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dpart += __uint_as_float(ov[e] << 16) * __uint_as_float(dv[e] << 16);
+        dpart += __uint_as_float(ov[e] & 0xffff0000u) * __uint_as_float(dv[e] & 0xffff0000u);
+      }
     }
   }
   const float nlse2 = -LSE[(size_t)head * N + qc] * kLog2e;
-  const float drow = Dvec[(size_t)head * N + qc];
+  const float drow = halves_sum(dpart);
+  if (hi == 0 && qrow < N) Dvec[(size_t)head * N + qrow] = drow;
 
   // Per-lane LDS offsets (the swizzle only looks at bits 0-3 of the row, so
   // 16- and 32-row steps are immediates): row-major reads of row l32 (K and
@@ -619,12 +607,15 @@ static hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_
                              const uint16_t* o, const uint16_t* dout, const float* lse,
                              uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec, int BH,
                              int N, float scale, hipStream_t stream) {
-  const long long rows = (long long)BH * N;
   const int xcd_group = (BH % 8 == 0) ? BH / 8 : 0;
   {
-    constexpr int RPB = 256 / (D / 8);
-    dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), grid, dim3(256), 0, stream, o, dout, dvec, rows);
+    // dQ first: it also writes D, which the dK / dV kernel reads.
+    using C = DqCfg<D>;
+    const int ntq = (N + C::BM - 1) / C::BM;
+    dim3 grid((unsigned)(ntq * BH));
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), grid, dim3(C::THREADS), 0, stream,
+                       q, k, v, dout, o, lse, dvec, dq, BH, N, ntq, scale * kLog2e, scale,
+                       xcd_group);
   }
   {
     using C = BwdCfg<D>;
@@ -633,14 +624,6 @@ static hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     dim3 grid((unsigned)(nunits * BH));
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(C::THREADS), 0, stream,
                        q, k, v, dout, lse, dvec, dk, dv, BH, N, nunits, scale * kLog2e, scale,
-                       xcd_group);
-  }
-  {
-    using C = DqCfg<D>;
-    const int ntq = (N + C::BM - 1) / C::BM;
-    dim3 grid((unsigned)(ntq * BH));
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), grid, dim3(C::THREADS), 0, stream,
-                       q, k, v, dout, lse, dvec, dq, BH, N, ntq, scale * kLog2e, scale,
                        xcd_group);
   }
   return hipGetLastError();
