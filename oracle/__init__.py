@@ -26,6 +26,9 @@ lesson 1 = page 1; the aiworkagent interview answer on FlashAttention = page 2;
   (the two-block example of page 3 section 19.5).
 * ``attention_fwd_brute`` / ``attention_bwd_brute`` -- scalar loops, no BLAS,
   for tiny inputs.
+* ``attention_decode`` -- the same definition with Nq query rows against Nk
+  key/value rows (the KV-cache use that page 2's bonus points name); causal
+  queries are the last Nq positions.
 
 Every function has a pin in ``tests/test_oracle.py`` that does not re-type its
 formula: closed forms, the worked example, invariants, brute force, central
@@ -33,6 +36,7 @@ finite differences and a library cross-check. No function is parity unpinned.
 """
 from .attention import (  # noqa: F401
     attention_bwd,
+    attention_decode,
     attention_bwd_brute,
     attention_fwd,
     attention_fwd_brute,

@@ -92,6 +92,30 @@ def attention_fwd(q, k, v, scale: float, causal: bool = False,
     return o.reshape(lead + qh.shape[1:]), lse.reshape(lead + (qh.shape[1],))
 
 
+def attention_decode(q, k, v, scale: float, causal: bool = False):
+    """Attention of Nq query rows against Nk key/value rows (a KV cache).
+
+    The plain definition of page 1 section 1 with a rectangular S (Nq x Nk);
+    the interview answer's bonus point names this use (inference with a KV
+    cache). ``causal``: the queries are the last Nq positions of the
+    sequence, so query i (position Nk - Nq + i) may attend key j iff
+    j <= Nk - Nq + i; with Nq = Nk this is the square causal mask above.
+    q: [..., Nq, d]; k, v: [..., Nk, d]. Returns (O [..., Nq, d], LSE [..., Nq])."""
+    qh, kh, vh = _heads(q), _heads(k), _heads(v)
+    lead = np.shape(q)[:-2]
+    nq, nk = qh.shape[1], kh.shape[1]
+    if causal and nq > nk:
+        raise ValueError("causal decode needs Nq <= Nk")
+    o = np.empty_like(qh)
+    lse = np.empty(qh.shape[:2])
+    for h in range(qh.shape[0]):
+        s = _scores(qh[h], kh[h], scale, causal, row0=nk - nq)
+        l_rows = _row_lse(s)
+        o[h] = np.exp(s - l_rows[:, None]) @ vh[h]
+        lse[h] = l_rows
+    return o.reshape(lead + qh.shape[1:]), lse.reshape(lead + (nq,))
+
+
 def _bwd_one_head(q, k, v, do, scale, causal, row_block):
     n = q.shape[0]
     dq = np.zeros_like(q)

@@ -331,3 +331,61 @@ def test_planted_wrong_mask_fails_row_zero_pin():
     wrong = np.where(np.arange(8)[None, :] < np.arange(8)[:, None] + 2, s, -np.inf)  # j <= i+1
     p = np.exp(wrong - wrong.max(1, keepdims=True)); p /= p.sum(1, keepdims=True)
     assert abs(p[0, 0] - 1.0) > 1e-3  # the pin demands p[0,0] == 1 (O_0 == V_0)
+
+
+# ---------------------------------------------------------------- decode (Nq x Nk)
+@pytest.mark.parametrize("nq", [1, 3, 16])
+def test_decode_rows_are_the_last_rows_of_causal_attention(nq):
+    """Causal decode of the last Nq queries equals the last Nq rows of the
+    full (square, pinned) causal attention over the same sequence."""
+    rng = np.random.default_rng(70 + nq)
+    n, d = 40, 8
+    q, k, v = (rng.standard_normal((2, n, d)) for _ in range(3))
+    o_full, l_full = oracle.attention_fwd(q, k, v, 0.4, causal=True)
+    o, l = oracle.attention_decode(q[:, n - nq:], k, v, 0.4, causal=True)
+    assert np.abs(o - o_full[:, n - nq:]).max() < 1e-12
+    assert np.abs(l - l_full[:, n - nq:]).max() < 1e-12
+
+
+def test_decode_noncausal_matches_scalar_loops():
+    """Rectangular non-causal case against scalar loops over every key."""
+    rng = np.random.default_rng(71)
+    nq, nk, d = 3, 11, 5
+    q, k, v = rng.standard_normal((nq, d)), rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    o, l = oracle.attention_decode(q, k, v, 0.7, causal=False)
+    for i in range(nq):
+        s = [0.7 * sum(float(q[i, c]) * float(k[j, c]) for c in range(d)) for j in range(nk)]
+        mx = max(s)
+        tot = sum(math.exp(x - mx) for x in s)
+        assert abs(l[i] - (mx + math.log(tot))) < 1e-12
+        for c in range(d):
+            ref = sum(math.exp(s[j] - mx) / tot * float(v[j, c]) for j in range(nk))
+            assert abs(o[i, c] - ref) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_scale_zero_closed_form(causal):
+    """scale = 0: every admissible key has weight 1/count, so O is the mean of
+    the admissible V rows and LSE = ln(count); query i of Nq (causal) admits
+    keys 0 .. Nk - Nq + i."""
+    rng = np.random.default_rng(72)
+    nq, nk, d = 4, 9, 3
+    q, k, v = rng.standard_normal((nq, d)), rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    o, l = oracle.attention_decode(q, k, v, 0.0, causal=causal)
+    for i in range(nq):
+        cnt = (nk - nq + i + 1) if causal else nk
+        assert np.abs(o[i] - v[:cnt].mean(axis=0)).max() < 1e-12
+        assert abs(l[i] - math.log(cnt)) < 1e-12
+
+
+def test_planted_decode_offset_mistake_fails_last_rows_pin(monkeypatch):
+    """A query offset one position off (row0 = Nk - Nq + 1) must fail the
+    last-rows pin."""
+    orig = oa._scores
+
+    def shifted(q, k, scale, causal, row0=0):
+        return orig(q, k, scale, causal, row0=row0 + 1 if q.shape[0] != k.shape[0] else row0)
+
+    monkeypatch.setattr(oa, "_scores", shifted)
+    with pytest.raises(AssertionError):
+        test_decode_rows_are_the_last_rows_of_causal_attention(3)
