@@ -41,6 +41,9 @@ def parse():
                    help="approximate CPU time budget of the oracle sample")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--decode", choices=["d1", "d8"], default=None,
+                   help="instead of the fused step, time decode attention (Nq query rows "
+                        "against a KV cache) on this decode workload; HBM-bound")
     p.add_argument("--unfused", action="store_true",
                    help="also time the unfused comparator (S and P in device memory) on the "
                         "same forward inputs and report the fused forward's speedup over it")
@@ -110,6 +113,89 @@ def cpu_baseline(w, inp, budget_s):
     }
 
 
+def run_decode(args):
+    """Decode attention: value = K/V bytes read per call / call time (GB/s)."""
+    import numpy as np
+    import torch
+    from exact_io_aware_12_amd import fa
+    from exact_io_aware_12_amd import inputs as fi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.library()
+    dev = torch.device("cuda:0")
+    w = fi.DECODE_WORKLOADS[args.decode]
+    qb, kb, vb = fi.make_decode_inputs(w)
+
+    def gpu(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = gpu(qb), gpu(kb), gpu(vb)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), device=dev, dtype=torch.float32)
+    ws = torch.empty(fa.fa_decode_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d), device=dev,
+                     dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        fa.decode_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = w.kv_bytes() / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "decode attention K/V read bandwidth (bf16, d=128)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "pass": "decode"},
+        "decode": {"avg_ms": round(ms, 4), "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "fa_decode_fwd (kernels fa_decode_kernel, fa_decode_merge_kernel)",
+                     "avg_launch_ms": round(ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from exact_io_aware_12_amd.inputs import bf16_bits_to_f64
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        done, t_total = 0, 0.0
+        for b, h in heads:
+            qq, kk, vv = (bf16_bits_to_f64(x[b, h]) for x in (qb, kb, vb))
+            t_s = time.perf_counter()
+            oracle.attention_decode(qq, kk, vv, w.scale, w.causal)
+            t_total += time.perf_counter() - t_s
+            done += 1
+            if t_total >= args.cpu_seconds:
+                break
+        per_head = w.kv_bytes() / len(heads)
+        rec["cpu_baseline"] = {"value": round(per_head * done / t_total / 1e9, 3), "unit": "GB/s",
+                               "cores": os.cpu_count() or 1, "kind": "oracle",
+                               "sample": f"{done} of {len(heads)} heads in fp64 (numpy), "
+                                         f"{t_total:.2f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -118,6 +204,10 @@ def main():
               "(attention shards by head with no exchange; see the design notes). "
               f"Asked for --gpus {args.gpus} (WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.decode is not None:
+        run_decode(args)
+        return
 
     import numpy as np
     import torch

@@ -19,6 +19,10 @@ hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 hipError_t unfused_fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 uint16_t* o, float* lse, float* ws, int BH, int N, int d,
                                 float scale, bool causal, hipStream_t stream, bool* blas_failed);
+int decode_splits(int BH, int Nk, int* chunk);
+hipError_t decode_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                           float* lse, float* ws, int BH, int Nq, int Nk, int d, float scale,
+                           bool causal, hipStream_t stream);
 }  // namespace fa
 
 namespace {
@@ -109,6 +113,42 @@ int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* 
       static_cast<float*>(workspace), B * H, N, d, scale, causal != 0,
       static_cast<hipStream_t>(stream), &blas_failed);
   if (blas_failed) return FA_ERR_BLAS;
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+static int check_decode(int B, int H, int Nq, int Nk, int d, int causal) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (Nq > 32 || (causal && Nq > Nk)) return FA_ERR_SHAPE;
+  if ((int64_t)B * H * Nk * d > kMaxElems) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  if (check_decode(B, H, Nq, Nk, d, 0) != FA_OK) return 0;
+  int chunk = 0;
+  const size_t ns = (size_t)fa::decode_splits(B * H, Nk, &chunk);
+  const size_t rows = (size_t)B * H * ns * Nq;
+  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+int fa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+                  float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int rc = check_decode(B, H, Nq, Nk, d, causal);
+  if (rc != FA_OK) return rc;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const size_t need = fa_decode_workspace_bytes(B, H, Nq, Nk, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, lse, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  hipError_t e = fa::decode_dispatch(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+      static_cast<float*>(workspace), B * H, Nq, Nk, d, scale, causal != 0,
+      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -7,8 +7,9 @@ PyTorch only supplies device memory and the stream. There is no fallback: if
 the library cannot be loaded, every call raises.
 
 The functions ``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes``,
-``fa_unfused_fwd``, ``fa_unfused_workspace_bytes`` and ``fa_strerror`` are the
-raw C entry points (ctypes). ``fwd`` / ``bwd`` / ``unfused_fwd`` are
+``fa_unfused_fwd``, ``fa_unfused_workspace_bytes``, ``fa_decode_fwd``,
+``fa_decode_workspace_bytes`` and ``fa_strerror`` are the raw C entry points
+(ctypes). ``fwd`` / ``bwd`` / ``unfused_fwd`` / ``decode_fwd`` are
 tensor-level wrappers with the same semantics.
 """
 from __future__ import annotations
@@ -59,6 +60,10 @@ def _load():
     lib.fa_unfused_workspace_bytes.restype = sz
     lib.fa_unfused_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
     lib.fa_unfused_fwd.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
+    lib.fa_decode_fwd.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -93,6 +98,16 @@ def fa_unfused_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scal
 
 def fa_unfused_workspace_bytes(B, H, N, d) -> int:
     return _load().fa_unfused_workspace_bytes(B, H, N, d)
+
+
+def fa_decode_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale, causal,
+                  stream) -> int:
+    return _load().fa_decode_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d,
+                                 scale, int(causal), stream)
+
+
+def fa_decode_workspace_bytes(B, H, Nq, Nk, d) -> int:
+    return _load().fa_decode_workspace_bytes(B, H, Nq, Nk, d)
 
 
 def fa_strerror(code: int) -> str:
@@ -212,4 +227,39 @@ def unfused_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, ou
                         causal, _stream_ptr(q.device, stream))
     if rc != FA_OK:
         raise FAError(rc, "fa_unfused_fwd")
+    return out, lse
+
+
+def decode_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None,
+               lse=None, workspace=None, stream=None):
+    """O, LSE of Nq <= 32 query rows ``q`` [B,H,Nq,d] against the key/value
+    cache ``k``, ``v`` [B,H,Nk,d] (bf16); causal queries are the last Nq
+    positions."""
+    import torch
+    _check(q, "q", dtype=torch.bfloat16)
+    _check(k, "k", dtype=torch.bfloat16)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected {(B, H, Nk, d)}")
+    _check(v, "v", k.shape, torch.bfloat16)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    _check(out, "out", q.shape, torch.bfloat16)
+    _check(lse, "lse", (B, H, Nq), torch.float32)
+    need = fa_decode_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _check(workspace, "workspace")
+    rc = fa_decode_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       B, H, Nq, Nk, d, float(scale), causal, _stream_ptr(q.device, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_decode_fwd")
     return out, lse

@@ -137,3 +137,47 @@ def random_bf16(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     if scale != 1.0:
         x = (x * np.float32(scale)).astype(np.float32)
     return f32_to_bf16_bits(x)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq query rows against an Nk-row key/value cache per (batch, head)."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V (bf16): what one call must read at least."""
+        return 2 * self.B * self.H * self.Nk * self.d * 2
+
+    def flops(self) -> float:
+        """4*B*H*Nq*Nk*d (two Nq x Nk x d contractions; the causal mask of the
+        last Nq positions removes a negligible triangle)."""
+        return 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+
+
+# Decode workloads (the pages give none; these stand for one or eight new
+# tokens per sequence against an 8192-token cache, 8 sequences x 32 heads).
+DECODE_WORKLOADS = {
+    "d1": DecodeWorkload("decode_b8h32_q1_k8192_d128", 8, 32, 1, 8192, 128, True, seed=11),
+    "d8": DecodeWorkload("decode_b8h32_q8_k8192_d128", 8, 32, 8, 8192, 128, True, seed=12),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload):
+    """Seeded draws for a decode workload: Q [B,H,Nq,d], then K and V
+    [B,H,Nk,d], each standard normal float32 rounded to bf16 bits."""
+    rng = np.random.default_rng(w.seed)
+    q = f32_to_bf16_bits(rng.standard_normal((w.B, w.H, w.Nq, w.d), dtype=np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((w.B, w.H, w.Nk, w.d), dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((w.B, w.H, w.Nk, w.d), dtype=np.float32))
+    return q, k, v

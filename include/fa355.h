@@ -126,6 +126,28 @@ FA355_API int fa_unfused_fwd(const void* q, const void* k, const void* v, void* 
            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
            float scale, int causal, void* stream);
 
+/*
+ * Decode attention: Nq (1..32) query rows against an Nk-row key/value cache
+ * per (batch, head) -- the KV-cache use named in the interview answer's bonus
+ * points -- with the same exact softmax as fa_fwd. The keys are split over
+ * many workgroups; each keeps the online-softmax statistics of lesson 1,
+ * sections 3-4 over its split, and a second kernel merges the partial
+ * results: LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+ *   q, o      : bf16 [B,H,Nq,d] (in, out)
+ *   k, v      : bf16 [B,H,Nk,d] (in)
+ *   lse       : out, fp32 [B,H,Nq]
+ *   causal    : the queries are the last Nq positions: query i may attend
+ *               keys 0 .. Nk-Nq+i (requires Nq <= Nk)
+ *   workspace : device memory of at least fa_decode_workspace_bytes(...)
+ *               bytes for the per-split partial O (fp32) and LSE; contents on
+ *               entry ignored, on return unspecified.
+ * B*H*Nk*d must fit in 2^31 - 1 elements. Other conventions as for fa_fwd.
+ */
+FA355_API size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+FA355_API int fa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+           float scale, int causal, void* stream);
+
 /* A static, human-readable description of an FA_* code. */
 FA355_API const char* fa_strerror(int code);
 

@@ -32,7 +32,8 @@ def fa():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_strerror",
+    assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_fwd",
+                           "fa_decode_workspace_bytes", "fa_fwd", "fa_strerror",
                            "fa_unfused_fwd", "fa_unfused_workspace_bytes"]
 
 
@@ -182,3 +183,41 @@ def test_unfused_validation(fa):
     assert _unf(fa, N=0) == fa.FA_ERR_SHAPE
     assert _unf(fa, d=32) == fa.FA_ERR_HEADDIM
     assert _unf(fa, scale=math.nan) == fa.FA_ERR_SCALE
+
+
+# ---------------------------------------------------------------- decode
+def _dec(fa, ws=GOOD, ws_bytes=None, B=1, H=1, Nq=1, Nk=100, d=128, scale=0.1, causal=1,
+         **ptrs):
+    p = dict(q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_decode_workspace_bytes(B, H, Nq, Nk, d)
+    return fa.fa_decode_fwd(p["q"], p["k"], p["v"], p["o"], p["lse"], ws, ws_bytes, B, H, Nq,
+                            Nk, d, scale, causal, None)
+
+
+def test_decode_workspace_bytes(fa):
+    # per split: Nq*d fp32 partial O plus Nq fp32 LSE; the split count depends
+    # on B*H and Nk only
+    w1 = fa.fa_decode_workspace_bytes(1, 1, 1, 100, 128)
+    assert w1 == 512 + 256                      # 100 keys: one split (128 fp32 + 1 fp32)
+    assert fa.fa_decode_workspace_bytes(16, 32, 4, 8192, 128) > 0
+    assert fa.fa_decode_workspace_bytes(1, 1, 33, 100, 128) == 0   # Nq > 32
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 100, 96) == 0
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_decode_null_and_align(fa, which):
+    assert _dec(fa, **{which: None}) == fa.FA_ERR_NULL
+    assert _dec(fa, **{which: GOOD + 4}) == fa.FA_ERR_ALIGN
+
+
+def test_decode_validation(fa):
+    need = fa.fa_decode_workspace_bytes(1, 1, 1, 100, 128)
+    assert _dec(fa, ws=None) == fa.FA_ERR_WORKSPACE
+    assert _dec(fa, ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    assert _dec(fa, Nq=33, ws_bytes=1 << 20) == fa.FA_ERR_SHAPE
+    assert _dec(fa, Nq=8, Nk=4, ws_bytes=1 << 20) == fa.FA_ERR_SHAPE     # causal needs Nq <= Nk
+    assert _dec(fa, Nk=0, ws_bytes=1 << 20) == fa.FA_ERR_SHAPE
+    assert _dec(fa, d=80, ws_bytes=1 << 20) == fa.FA_ERR_HEADDIM
+    assert _dec(fa, scale=math.inf) == fa.FA_ERR_SCALE

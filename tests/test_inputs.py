@@ -51,3 +51,14 @@ def test_flop_counts():
     w5 = fi.WORKLOADS[5]
     assert w5.fwd_flops() == pytest.approx(34.359738368e9)
     assert w5.bwd_flops() == pytest.approx(85.89934592e9)
+
+
+def test_decode_inputs_are_seeded():
+    small = fi.DecodeWorkload("t", 1, 2, 3, 40, 64, True, seed=5)
+    a = fi.make_decode_inputs(small)
+    b = fi.make_decode_inputs(small)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    assert a[0].shape == (1, 2, 3, 64) and a[1].shape == (1, 2, 40, 64)
+    assert a[0].dtype == np.uint16
+    for w in fi.DECODE_WORKLOADS.values():
+        assert w.Nq <= 32 and (not w.causal or w.Nq <= w.Nk)
