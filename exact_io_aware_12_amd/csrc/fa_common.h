@@ -51,11 +51,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // log2(x) (v_log_f32).
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value held by lane (l ^ 32): the other half of the wave.
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
-}
-
 // max / sum of x over lanes l and l ^ 32, via v_permlane32_swap (one VALU
 // exchange, no LDS round trip): swapping x with itself leaves x of the low
 // half in one result and x of the high half in the other, on every lane.
@@ -85,27 +80,8 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Byte permute of the dword pair {hi_src, lo_src} (v_perm_b32): selector bytes
-// 0-3 pick bytes of lo_src, 4-7 bytes of hi_src.
-__device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
-}
-// Low 16-bit halves of a and b -> (b.lo << 16) | a.lo.
-__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
-  return perm_b32(b, a, 0x05040100u);
-}
-// High 16-bit halves of a and b -> (b.hi << 16) | a.hi.
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
-  return perm_b32(b, a, 0x07060302u);
-}
-
 __device__ __forceinline__ u32x4 ld_global_16B(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
-}
-
-__device__ __forceinline__ u32x4 zero_u32x4() {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return z;
 }
 
 }  // namespace fa

@@ -108,20 +108,6 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB]) {
   return r[0];
 }
 template <int NB>
-__device__ __forceinline__ float tile_min(const f32x16 (&s)[NB]) {
-  float r[NB * 4];
-#pragma unroll
-  for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      r[kb * 4 + g] = vmin(vmin(s[kb][4 * g], s[kb][4 * g + 1]), vmin(s[kb][4 * g + 2], s[kb][4 * g + 3]));
-#pragma unroll
-  for (int w = NB * 4; w > 1; w >>= 1)
-#pragma unroll
-    for (int i = 0; i < w / 2; ++i) r[i] = vmin(r[i], r[i + w / 2]);
-  return r[0];
-}
-template <int NB>
 __device__ __forceinline__ float tile_sum(const f32x16 (&s)[NB]) {
   float r[NB * 4];
 #pragma unroll
