@@ -244,3 +244,25 @@ def test_workload5_fwd_bwd(fa):
                                      w.scale, True)
             for name, got, ref in zip(("dQ", "dK", "dV"), g, r):
                 assert_close(f"{name}[{b},{h}]", got[b, h], ref, TOL_GRAD)
+
+
+# ---------------------------------------------------------------- long context
+@pytest.mark.parametrize("N,H,d", [(65536, 2, 128), (100003, 1, 64)])
+def test_fwd_long_context_sampled_rows(fa, N, H, d):
+    """Long sequences (64-bit offsets, 1000+ key tiles per query tile, a ragged
+    tail at N = 100003): sampled rows of the causal forward against the
+    oracle's definition for each row (that query against keys 0..i)."""
+    import torch
+    print(f"[long] H={H} N={N} d={d}", flush=True)
+    shape = (1, H, N, d)
+    qb, kb, vb = (fi.random_bf16(shape, 60 + i) for i in range(3))
+    scale = 1 / math.sqrt(d)
+    o, lse, _ = _run_fwd(fa, qb, kb, vb, scale, True)
+    o_np, l_np = from_gpu(o), from_gpu(lse)
+    rows = [0, 1, 63, 64, 127, 128, 4095, N // 2, N - 129, N - 64, N - 2, N - 1]
+    for h in range(H):
+        q, k, v = bits_to_f64(qb[0, h]), bits_to_f64(kb[0, h]), bits_to_f64(vb[0, h])
+        for i in rows:
+            ro, rl = oracle.attention_decode(q[i:i + 1], k[:i + 1], v[:i + 1], scale, False)
+            assert_close(f"O[{h},{i}]", o_np[0, h, i:i + 1], ro, TOL_O)
+            assert_close(f"LSE[{h},{i}]", l_np[0, h, i:i + 1], rl, TOL_LSE)
