@@ -80,3 +80,8 @@ def test_decode_deterministic(fa):
     o2, l2 = fa.decode_fwd(q, k, v, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_long_cache_many_splits(fa):
+    """A 500000-key cache on one head: about 2000 key splits merged."""
+    _check(fa, 1, 1, 4, 500000, 128, True, seed=61)
