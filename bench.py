@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--unfused", action="store_true",
                    help="also time the unfused comparator (S and P in device memory) on the "
                         "same forward inputs and report the fused forward's speedup over it")
+    p.add_argument("--fa1", action="store_true",
+                   help="also time the loop-order comparator (outer loop over key/value "
+                        "tiles, one workgroup per head) on the same forward inputs")
     return p.parse_args()
 
 
@@ -313,6 +316,37 @@ def main():
                            "full N x N is computed also when causal"}
         del ws_u
 
+    fa1 = None
+    if args.fa1:
+        ws_1 = torch.empty(fa.fa_fa1_workspace_bytes(w.B, w.H, w.N, w.d), device=dev,
+                           dtype=torch.uint8)
+        o_1 = torch.empty_like(q)
+        lse_1 = torch.empty_like(lse)
+
+        def fwd1():
+            fa.fa1_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o_1, lse=lse_1,
+                       workspace=ws_1)
+
+        fwd1()
+        torch.cuda.synchronize()
+        n_1 = max(2, min(args.steps, 10))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_1):
+            fwd1()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        a_ms = e0.elapsed_time(e1) / n_1
+        fa1 = {"avg_ms": round(a_ms, 4), "calls": n_1,
+               "fwd_tflops_equiv": round(w.fwd_flops() / (a_ms * 1e-3) / 1e12, 2),
+               "fused_fwd_speedup": round(a_ms / f_avg, 2),
+               "workgroups": w.B * w.H,
+               "workspace_GB": round(ws_1.numel() / 1e9, 3),
+               "note": "outer loop over 64-key tiles, inner over 128-row query tiles; the "
+                       "running O, max and sum of every query tile round-trip device memory "
+                       "once per (key tile, query tile) pair"}
+        del ws_1
+
     if args.copy_calib_mib > 0:
         src = torch.empty(args.copy_calib_mib * 2 ** 20, device=dev, dtype=torch.uint8)
         dst = torch.empty_like(src)
@@ -348,6 +382,8 @@ def main():
                       "hbm_alg_GBs": round(bwd_bytes(w) / (b_avg * 1e-3) / 1e9, 1)}
     if unfused is not None:
         rec["unfused"] = unfused
+    if fa1 is not None:
+        rec["fa1_order"] = fa1
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -19,6 +19,10 @@ hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 hipError_t unfused_fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 uint16_t* o, float* lse, float* ws, int BH, int N, int d,
                                 float scale, bool causal, hipStream_t stream, bool* blas_failed);
+size_t fa1_workspace_floats(int BH, int N, int d);
+hipError_t fa1_fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            uint16_t* o, float* lse, float* ws, int BH, int N, int d,
+                            float scale, bool causal, hipStream_t stream);
 int decode_splits(int BH, int Nk, int* chunk);
 hipError_t decode_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                            float* lse, float* ws, int BH, int Nq, int Nk, int d, float scale,
@@ -116,6 +120,31 @@ int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_fa1_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  return round256(fa::fa1_workspace_floats(B * H, N, d) * sizeof(float));
+}
+
+int fa_fa1_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               void* workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale,
+               int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != FA_OK) return rc;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const size_t need = fa_fa1_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, lse, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  hipError_t e = fa::fa1_fwd_dispatch(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+      static_cast<float*>(workspace), B * H, N, d, scale, causal != 0,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 static int check_decode(int B, int H, int Nq, int Nk, int d, int causal) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
@@ -160,7 +189,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
-    case FA_ERR_WORKSPACE: return "backward workspace is NULL or too small";
+    case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case FA_ERR_HIP: return "the HIP runtime reported a launch error";
     case FA_ERR_BLAS: return "rocBLAS reported an error (unfused comparator only)";
     default: return "unknown fa355 error code";

@@ -7,9 +7,10 @@ PyTorch only supplies device memory and the stream. There is no fallback: if
 the library cannot be loaded, every call raises.
 
 The functions ``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes``,
-``fa_unfused_fwd``, ``fa_unfused_workspace_bytes``, ``fa_decode_fwd``,
+``fa_unfused_fwd``, ``fa_unfused_workspace_bytes``, ``fa_fa1_fwd``,
+``fa_fa1_workspace_bytes``, ``fa_decode_fwd``,
 ``fa_decode_workspace_bytes`` and ``fa_strerror`` are the raw C entry points
-(ctypes). ``fwd`` / ``bwd`` / ``unfused_fwd`` / ``decode_fwd`` are
+(ctypes). ``fwd`` / ``bwd`` / ``unfused_fwd`` / ``fa1_fwd`` / ``decode_fwd`` are
 tensor-level wrappers with the same semantics.
 """
 from __future__ import annotations
@@ -60,6 +61,10 @@ def _load():
     lib.fa_unfused_workspace_bytes.restype = sz
     lib.fa_unfused_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
     lib.fa_unfused_fwd.restype = i
+    lib.fa_fa1_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_fa1_workspace_bytes.restype = sz
+    lib.fa_fa1_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    lib.fa_fa1_fwd.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
@@ -98,6 +103,16 @@ def fa_unfused_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scal
 
 def fa_unfused_workspace_bytes(B, H, N, d) -> int:
     return _load().fa_unfused_workspace_bytes(B, H, N, d)
+
+
+def fa_fa1_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale, causal,
+               stream) -> int:
+    return _load().fa_fa1_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d,
+                              float(scale), int(bool(causal)), stream)
+
+
+def fa_fa1_workspace_bytes(B, H, N, d) -> int:
+    return _load().fa_fa1_workspace_bytes(B, H, N, d)
 
 
 def fa_decode_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale, causal,
@@ -198,10 +213,8 @@ def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None
     return dq, dk, dv
 
 
-def unfused_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None,
-                lse=None, workspace=None, stream=None):
-    """The same O, LSE as ``fwd`` by the unfused three-step method (S and P in
-    device memory): the measured comparator of the fused pass."""
+def _fwd_with_workspace(q, k, v, causal, scale, out, lse, workspace, stream, raw, ws_bytes,
+                        name):
     import torch
     _check(q, "q", dtype=torch.bfloat16)
     if q.dim() != 4:
@@ -217,17 +230,33 @@ def unfused_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, ou
         lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
     _check(out, "out", q.shape, torch.bfloat16)
     _check(lse, "lse", (B, H, N), torch.float32)
-    need = fa_unfused_workspace_bytes(B, H, N, d)
+    need = ws_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     _check(workspace, "workspace")
-    rc = fa_unfused_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                        lse.data_ptr(), workspace.data_ptr(),
-                        workspace.numel() * workspace.element_size(), B, H, N, d, float(scale),
-                        causal, _stream_ptr(q.device, stream))
+    rc = raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+             workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, N, d,
+             float(scale), causal, _stream_ptr(q.device, stream))
     if rc != FA_OK:
-        raise FAError(rc, "fa_unfused_fwd")
+        raise FAError(rc, name)
     return out, lse
+
+
+def unfused_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None,
+                lse=None, workspace=None, stream=None):
+    """The same O, LSE as ``fwd`` by the unfused three-step method (S and P in
+    device memory): the measured comparator of the fused pass."""
+    return _fwd_with_workspace(q, k, v, causal, scale, out, lse, workspace, stream,
+                               fa_unfused_fwd, fa_unfused_workspace_bytes, "fa_unfused_fwd")
+
+
+def fa1_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None,
+            lse=None, workspace=None, stream=None):
+    """The same O, LSE as ``fwd`` with the loop order swapped (outer loop over
+    key/value tiles, one workgroup per head, running state in device memory):
+    the measured loop-order comparator of the fused pass."""
+    return _fwd_with_workspace(q, k, v, causal, scale, out, lse, workspace, stream,
+                               fa_fa1_fwd, fa_fa1_workspace_bytes, "fa_fa1_fwd")
 
 
 def decode_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None,

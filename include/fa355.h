@@ -60,7 +60,7 @@ enum {
   FA_ERR_HEADDIM = 3,   /* d is not 64 or 128                                */
   FA_ERR_SCALE = 4,     /* scale is NaN or infinite                          */
   FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                  */
-  FA_ERR_WORKSPACE = 6, /* backward workspace NULL or smaller than required  */
+  FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required           */
   FA_ERR_HIP = 7,       /* the HIP runtime reported a launch error           */
   FA_ERR_BLAS = 8       /* rocBLAS reported an error (fa_unfused_fwd only)   */
 };
@@ -146,6 +146,25 @@ FA355_API int fa_unfused_fwd(const void* q, const void* k, const void* v, void* 
 FA355_API size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 FA355_API int fa_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+           float scale, int causal, void* stream);
+
+/*
+ * The same O and LSE as fa_fwd computed in the other loop order, kept as a
+ * measured comparator: the outer loop runs over key/value tiles and the inner
+ * loop over query tiles (the interview answer's bonus points; "FlashAttention
+ * and Triton", section 19.7 on the move from the first to the second
+ * version). One workgroup handles one (batch, head); between key tiles each
+ * query tile's unnormalised output and its running max and sum live in the
+ * workspace, read and rewritten once per (key tile, query tile) pair with the
+ * online-softmax rescaling of lesson 1, section 3.
+ *   q, k, v, o, lse : as for fa_fwd
+ *   workspace       : device memory of at least fa_fa1_workspace_bytes(...)
+ *                     bytes (fp32 running state of every query row); contents
+ *                     on entry ignored, on return unspecified.
+ */
+FA355_API size_t fa_fa1_workspace_bytes(int B, int H, int N, int d);
+FA355_API int fa_fa1_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
            float scale, int causal, void* stream);
 
 /* A static, human-readable description of an FA_* code. */

@@ -33,8 +33,9 @@ def fa():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_fwd",
-                           "fa_decode_workspace_bytes", "fa_fwd", "fa_strerror",
-                           "fa_unfused_fwd", "fa_unfused_workspace_bytes"]
+                           "fa_decode_workspace_bytes", "fa_fa1_fwd", "fa_fa1_workspace_bytes",
+                           "fa_fwd", "fa_strerror", "fa_unfused_fwd",
+                           "fa_unfused_workspace_bytes"]
 
 
 def test_every_declared_symbol_is_exported():
@@ -183,6 +184,44 @@ def test_unfused_validation(fa):
     assert _unf(fa, N=0) == fa.FA_ERR_SHAPE
     assert _unf(fa, d=32) == fa.FA_ERR_HEADDIM
     assert _unf(fa, scale=math.nan) == fa.FA_ERR_SCALE
+
+
+# ---------------------------------------------------------------- loop-order comparator
+def _fa1(fa, ws=GOOD, ws_bytes=None, B=1, H=1, N=16, d=64, scale=0.125, **ptrs):
+    p = dict(q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_fa1_workspace_bytes(1, 1, 16, 64)
+    return fa.fa_fa1_fwd(p["q"], p["k"], p["v"], p["o"], p["lse"], ws, ws_bytes, B, H, N, d,
+                         scale, 1, None)
+
+
+def test_fa1_workspace_bytes(fa):
+    """fp32 running state per (head, 128-row query tile, wave of 32 rows): the
+    O^T accumulator (d/2 registers) plus the running max and sum, 64 lanes
+    each."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    for B, H, N, d in [(1, 1, 1, 64), (2, 3, 129, 128), (1, 16, 16384, 128), (4, 16, 1000, 64)]:
+        ntq = (N + 127) // 128
+        assert fa.fa_fa1_workspace_bytes(B, H, N, d) == r256(B * H * ntq * 4 * (d // 2 + 2) * 64 * 4)
+    assert fa.fa_fa1_workspace_bytes(1, 0, 8, 64) == 0
+    assert fa.fa_fa1_workspace_bytes(1, 1, 8, 96) == 0
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_fa1_null_and_align(fa, which):
+    assert _fa1(fa, **{which: None}) == fa.FA_ERR_NULL
+    assert _fa1(fa, **{which: GOOD + 4}) == fa.FA_ERR_ALIGN
+
+
+def test_fa1_validation(fa):
+    need = fa.fa_fa1_workspace_bytes(1, 1, 16, 64)
+    assert _fa1(fa, ws=None) == fa.FA_ERR_WORKSPACE
+    assert _fa1(fa, ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    assert _fa1(fa, ws=GOOD + 8) == fa.FA_ERR_ALIGN
+    assert _fa1(fa, N=0) == fa.FA_ERR_SHAPE
+    assert _fa1(fa, d=32) == fa.FA_ERR_HEADDIM
+    assert _fa1(fa, scale=math.inf) == fa.FA_ERR_SCALE
 
 
 # ---------------------------------------------------------------- decode
