@@ -162,8 +162,11 @@ def _check_bwd(fa, B, H, N, d, causal, seed, scale=None):
     assert_close("dV", from_gpu(dv), rv, TOL_GRAD)
 
 
-BWD_SMALL = [(1, 1, 1), (1, 1, 5), (1, 2, 64), (2, 1, 129), (1, 3, 300), (1, 8, 512),
-             (1, 1, 1000)]
+# Causal dQ pairs query tiles (u, ntq-1-u) and splits the pair's key tiles
+# between two wave groups: ntq = 1 (one group idle or a lone split tile),
+# 2 with no split (N = 130), odd ntq (a middle tile split alone), ragged ends.
+BWD_SMALL = [(1, 1, 1), (1, 1, 5), (1, 2, 64), (2, 1, 129), (1, 2, 130), (1, 3, 300),
+             (1, 8, 512), (1, 1, 577), (1, 1, 1000)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
