@@ -1,4 +1,5 @@
-"""Build libfa355.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+"""Build libfa355.so (the HIP kernels and the C ABI) for gfx950, in-tree, and
+the fa355_ceilings calibration program.
 
 Usage: ``python -m exact_io_aware_12_amd.build`` (or ``__graft_entry__.build()``).
 Always recompiles. Needs only hipcc; no GPU is touched.
@@ -15,6 +16,9 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa355.so")
+# Calibration program (unit ceilings measured on the device), not linked into
+# the library.
+CEILINGS = os.path.join(PKG, "fa355_ceilings")
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_unfused.hip", "fa_fa1.hip", "fa_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -49,6 +53,12 @@ def build(extra: list[str] | None = None) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
         os.replace(out_tmp, LIB)
+        cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, os.path.join(CSRC, "ceilings.hip"), "-o",
+               CEILINGS + ".tmp"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for ceilings.hip:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(CEILINGS + ".tmp", CEILINGS)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
     return LIB
