@@ -12,7 +12,11 @@
 //   1. fa_bwd_dq:    D_i = dO_i . O_i (written out) and dQ. One workgroup per
 //      128-query tile (4 wave64s x 32 queries, two workgroups per CU); the
 //      loop runs over 64-key tiles and recomputes S and dP (inner loop over
-//      K/V, so dQ stays in registers).
+//      K/V, so dQ stays in registers). When the causal grid fits in one
+//      round, each workgroup instead holds two such groups of 4 waves that
+//      take alternate key tiles of the same query tile, and their partial
+//      dQ are summed in LDS: the round is bound by the longest tile's chain
+//      of key tiles, which this halves.
 //   2. fa_bwd_dkdv:  dK and dV. One workgroup per key tile pair (8 wave64s,
 //      two per SIMD: 4 key blocks of 32 x 2 query halves); the loop runs over
 //      64-query tiles (outer loop over K/V, inner over Q, so dK and dV stay
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <int D>
 struct DqCfg {
   static constexpr int BM = 128;              // queries per workgroup (32 per wave)
-  static constexpr int THREADS = 256;         // 4 waves
+  static constexpr int THREADS = 256;         // 4 waves per key-tile group
   static constexpr int BN = 64;               // keys per tile
   static constexpr int RB = D * 2;            // bytes per K / V row in LDS
   static constexpr int TILE = BN * RB;        // 16 KiB (d=128)
@@ -409,20 +413,24 @@ struct DqCfg {
 };
 
 // dQ_i = scale * sum_j dS_ij K_j for one 128-query tile per workgroup.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
+template <int D, bool CAUSAL, int G>
+__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const uint16_t* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ Dvec,
     uint16_t* __restrict__ dQ, int BH, int N, int ntq, float c2, float scale, int xcd_group) {
   using C = DqCfg<D>;
   constexpr int KS = C::KS, DB = C::DB, NB = C::NB, RB = C::RB;
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[2][C::TILE];
+  // G groups of 4 waves share the query tile and split its key tiles (group
+  // g takes tiles g, g+G, ...), each with its own double buffer.
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[G][2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[G][2][C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wall = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = G == 1 ? 0 : wall >> 2;   // key-tile group
+  const int w = wall & 3;              // wave within the group (its 32 query rows)
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Workgroup -> (head, query tile): heaviest causal tiles first, the
@@ -450,8 +458,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Key tiles this wave computes: 0 .. ntw-1 (causal waves stop at the diagonal).
   const int ntw = CAUSAL ? min(nt, (min(N, qw + 32) + C::BN - 1) / C::BN) : nt;
 
-  dma_rows<D, C::LOADS>(K + off, k_lds[0], 0, N, w, lane);
-  dma_rows<D, C::LOADS>(V + off, v_lds[0], 0, N, w, lane);
+  dma_rows<D, C::LOADS>(K + off, k_lds[grp][0], min(grp, nt - 1) * C::BN, N, w, lane);
+  dma_rows<D, C::LOADS>(V + off, v_lds[grp][0], min(grp, nt - 1) * C::BN, N, w, lane);
 
   // This lane's Q and dO rows as B operands (k-slots = head dim), and its
   // row statistics: LSE in log2 units and D = dO . O (B1), summed over the
@@ -476,7 +484,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const float nlse2 = -LSE[(size_t)head * N + qc] * kLog2e;
   const float drow = halves_sum(dpart);
-  if (hi == 0 && qrow < N) Dvec[(size_t)head * N + qrow] = drow;
+  if (grp == 0 && hi == 0 && qrow < N) Dvec[(size_t)head * N + qrow] = drow;
 
   // Per-lane LDS offsets (the swizzle only looks at bits 0-3 of the row, so
   // 16- and 32-row steps are immediates): row-major reads of row l32 (K and
@@ -562,29 +570,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < nt; ++j) {
-    const int b = j & 1;
-    // Copies of K and V tile j+1 into the other buffers (copy c: K part c/2
-    // for even c, V part c/2 for odd c); on the last tile they repeat it (in
-    // bounds, unused).
-    const int kc = min(j + 1, nt - 1) * C::BN;
+  // Step s: group g computes key tile j = G*s + g and copies its next tile
+  // j + G into its other buffers (copy c: K part c/2 for even c, V part c/2
+  // for odd c); past the last tile the copies repeat it (in bounds, unused).
+  // Every group runs the same number of steps, so all waves meet the same
+  // barriers.
+  const int ns = (nt + G - 1) / G;
+  for (int s = 0; s < ns; ++s) {
+    const int b = s & 1;
+    const int j = G * s + grp;
+    const int kc = min(j + G, nt - 1) * C::BN;
     const bool full = kc + C::BN <= N;
     auto copy = [&](int c) __attribute__((always_inline)) {
       const int i = c >> 1;
-      uint8_t* dst = (c & 1) ? v_lds[b ^ 1] : k_lds[b ^ 1];
+      uint8_t* dst = (c & 1) ? v_lds[grp][b ^ 1] : k_lds[grp][b ^ 1];
       const uint16_t* src = ((c & 1) ? V : K) + off + (size_t)kc * D;
       lds_copy16s(src, full ? offd[i] : offr[i], lds_addr(dst + (w * C::LOADS + i) * 1024));
     };
     if (j < ntw) {
       const int kbase = j * C::BN;
       const bool masked = (CAUSAL && kbase + C::BN - 1 > qw) || kbase + C::BN > N;
-      tile(k_lds[b], v_lds[b], kbase, masked, copy);
+      tile(k_lds[grp][b], v_lds[grp][b], kbase, masked, copy);
     } else {
 #pragma unroll
       for (int c = 0; c < 2 * C::LOADS; ++c) copy(c);
     }
     wait_vmem();
     __syncthreads();
+  }
+
+  // ---- The two groups' partial dQ^T are summed through LDS (lane-contiguous
+  // fp32, in the K buffers: every read of them finished before the last
+  // barrier).
+  if constexpr (G == 2) {
+    float* red = reinterpret_cast<float*>(k_lds) + w * (DB * 16 * 64) + lane;
+    static_assert(4 * DB * 16 * 64 * 4 <= 2 * G * C::TILE, "partial sums fit the K buffers");
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[(db * 16 + i) * 64] = dqacc[db][i];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dqacc[db][i] += red[(db * 16 + i) * 64];
   }
 
   // ---- dQ = scale * dQ^T (one query per lane; 4 consecutive d per store).
@@ -613,9 +645,23 @@ static hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     using C = DqCfg<D>;
     const int ntq = (N + C::BM - 1) / C::BM;
     dim3 grid((unsigned)(ntq * BH));
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), grid, dim3(C::THREADS), 0, stream,
-                       q, k, v, dout, o, lse, dvec, dq, BH, N, ntq, scale * kLog2e, scale,
-                       xcd_group);
+    // A causal grid that fits in one round (two 4-wave workgroups per CU on
+    // 256 CUs) takes as long as its longest query tile's chain of key tiles:
+    // then each tile's key tiles are split over two groups of 4 waves in one
+    // workgroup (measured at B=2, H=16, N=2048: -5 us of about 150).
+    bool split = false;
+    if constexpr (CAUSAL) {
+      if (ntq * BH <= 512) {
+        split = true;
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, 2>), grid, dim3(2 * C::THREADS), 0,
+                           stream, q, k, v, dout, o, lse, dvec, dq, BH, N, ntq, scale * kLog2e,
+                           scale, xcd_group);
+      }
+    }
+    if (!split)
+      hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, 1>), grid, dim3(C::THREADS), 0, stream,
+                         q, k, v, dout, o, lse, dvec, dq, BH, N, ntq, scale * kLog2e, scale,
+                         xcd_group);
   }
   {
     using C = BwdCfg<D>;

@@ -162,9 +162,11 @@ def _check_bwd(fa, B, H, N, d, causal, seed, scale=None):
     assert_close("dV", from_gpu(dv), rv, TOL_GRAD)
 
 
-# Causal dQ pairs query tiles (u, ntq-1-u) and splits the pair's key tiles
-# between two wave groups: ntq = 1 (one group idle or a lone split tile),
-# 2 with no split (N = 130), odd ntq (a middle tile split alone), ragged ends.
+# Causal grids of at most 512 query tiles split each tile's key tiles between
+# two wave groups of one dQ workgroup (group g takes key tiles g, g+2, ...):
+# one key tile (the second group idle: N <= 64), odd and even key-tile
+# counts, ragged ends. Every causal case below takes that path; the
+# unsplit causal dQ is covered by test_bwd_causal_unsplit_grid.
 BWD_SMALL = [(1, 1, 1), (1, 1, 5), (1, 2, 64), (2, 1, 129), (1, 2, 130), (1, 3, 300),
              (1, 8, 512), (1, 1, 577), (1, 1, 1000)]
 
@@ -174,6 +176,13 @@ BWD_SMALL = [(1, 1, 1), (1, 1, 5), (1, 2, 64), (2, 1, 129), (1, 2, 130), (1, 3, 
 @pytest.mark.parametrize("B,H,N", BWD_SMALL)
 def test_bwd_small(fa, B, H, N, d, causal):
     _check_bwd(fa, B, H, N, d, causal, seed=2000 + N + d)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_causal_unsplit_grid(fa, d):
+    # 4 query tiles x 132 heads = 528 > 512: the causal dQ kernel without the
+    # key split; N = 500 leaves a ragged last tile.
+    _check_bwd(fa, 4, 33, 500, d, True, seed=2500 + d)
 
 
 def test_bwd_deterministic(fa):
