@@ -1,19 +1,31 @@
 // Ceilings of the units the attention kernels use, measured on the device:
 // a calibration program, not part of the library.
 //
-//   mfma   dense v_mfma_f32_32x32x16_bf16, four independent accumulators per
-//          wave (FLOP/s; the MFMA roof)
+//   mfma   dense v_mfma_f32_32x32x16_bf16, four (and eight) independent
+//          accumulators per wave (FLOP/s; the MFMA roof)
 //   exp    v_exp_f32 chains (8 independent per lane; each step is exp2 then a
 //          subtract, as in the softmax)
 //   fma    v_fma_f32 chains (8 independent per lane)
 //   lds    ds_read_b128 from a 64 KiB tile (bytes/s)
 //   mix    four MFMAs plus 8*k exp steps per loop iteration in the same
-//          wave, k = 0..4: how much exp work rides free under the MFMAs
+//          wave, k = 0..4, in the compiler's own order (it issues the MFMAs
+//          back to back, then the exps)
+//   mixil  eight MFMAs per iteration, each followed by E exp steps placed
+//          there by scheduling-group barriers: with the VALU mask alone
+//          (0x002, which does not take v_exp_f32) and with VALU |
+//          transcendental (0x402); how much exp work a wave runs under its
+//          own MFMAs when its stream interleaves them
+//   ldsmfma MFMAs whose A operand comes from LDS, as the attention kernels
+//          read K (ds_read_b128) or V^T (two ds_read_b64_tr_b16), each read
+//          feeding one or two MFMAs; the reads run half an iteration ahead
 //
 // Each is timed with HIP events at one and two 4-wave workgroups per CU (one
 // and two waves per SIMD), on 256 x {1,2} workgroups. Every kernel writes one
 // value per thread so the work is kept; grids and indexes stay in bounds by
-// construction (out has 512 * 256 floats; LDS indexes are masked to 4095).
+// construction (out has 512 * 256 floats; LDS indexes are masked to 4095 in
+// k_lds and stay below 32 KiB in k_ldsmfma).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 
@@ -49,6 +61,22 @@ __global__ __launch_bounds__(256) void k_mfma(float* out, int iters) {
   }
   float s = 0.f;
   for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mfma8(float* out, int iters) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(threadIdx.x * 0.001f);
+    b[i] = (__bf16)(i * 0.01f);
+  }
+  f32x16 c[8];
+  for (int i = 0; i < 8; ++i) for (int j = 0; j < 16; ++j) c[i][j] = 0.f;
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) c[m] = mfma(a, b, c[m]);
+  float s = 0.f;
+  for (int i = 0; i < 8; ++i) for (int j = 0; j < 16; ++j) s += c[i][j];
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
@@ -112,6 +140,93 @@ __global__ __launch_bounds__(256) void k_mix(float* out, int iters, int nexp) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+template <int E, int MASK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mixil(float* out, int iters) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(threadIdx.x * 0.001f);
+    b[i] = (__bf16)(i * 0.01f);
+  }
+  f32x16 c[8];
+  for (int i = 0; i < 8; ++i) for (int j = 0; j < 16; ++j) c[i][j] = 0.f;
+  float x[16];
+  for (int i = 0; i < 16; ++i) x[i] = -0.001f * (threadIdx.x + i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      c[m] = mfma(a, b, c[m]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = (m * E + e) & 15;
+        x[k] = __builtin_amdgcn_exp2f(x[k]) - 1.0f;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (E > 0) __builtin_amdgcn_sched_group_barrier(MASK, 2 * E, 0);
+    }
+  }
+  float s = 0.f;
+  for (int i = 0; i < 8; ++i) for (int j = 0; j < 16; ++j) s += c[i][j];
+  for (int i = 0; i < 16; ++i) s += x[i];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+template <int R, bool TR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ldsmfma(float* out, int iters) {
+  __shared__ __attribute__((aligned(1024))) unsigned char buf[32768];
+  for (int i = threadIdx.x; i < 32768 / 4; i += 256) reinterpret_cast<unsigned*>(buf)[i] = i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int g = lane >> 4, sl = lane & 15;
+  bf16x8 b[R];
+  for (int r = 0; r < R; ++r) for (int i = 0; i < 8; ++i) b[r][i] = (__bf16)((i + r) * 0.01f);
+  f32x16 c[4 * R];
+  for (int i = 0; i < 4 * R; ++i) for (int j = 0; j < 16; ++j) c[i][j] = 0.f;
+  // Operand i of a 16 KiB half: K pattern (row l32 of 32-key block i&1,
+  // XOR-swizzled 16-byte chunk 2*(i>>1)+hi) or V^T pattern (16 keys t = i>>2,
+  // 32 columns db = i&3, two transposing reads 8 rows apart); all < 16 KiB.
+  auto addr = [&](int i, int half) -> int {
+    if (!TR) {
+      const int kb = i & 1, ks = i >> 1;
+      return half * 16384 + (kb * 32 + l32) * 256 + (((2 * ks + hi) ^ (l32 & 15)) << 4);
+    } else {
+      const int t = i >> 2, db = i & 3;
+      const int row = 4 * hi + (sl >> 2), col = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
+      const int off = row * 256 + (((col >> 5) ^ (row & 3)) << 6) + (col & 31) * 2;
+      return half * 16384 + 16 * t * 256 + off;
+    }
+  };
+  auto rd = [&](int a) -> bf16x8 {
+    if (!TR) return *reinterpret_cast<const bf16x8*>(buf + a);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + a));
+    const s16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + a + 2048));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8 a0[8], a1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a0[i] = rd(addr(i, 0));
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a1[i] = rd(addr(8 + i, it & 1));
+#pragma unroll
+      for (int r = 0; r < R; ++r) c[(i & 3) * R + r] = mfma(a0[i], b[r], c[(i & 3) * R + r]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a0[i] = rd(addr(i, (it + 1) & 1));
+#pragma unroll
+      for (int r = 0; r < R; ++r) c[(i & 3) * R + r] = mfma(a1[i], b[r], c[(i & 3) * R + r]);
+    }
+  }
+  float s = 0.f;
+  for (int i = 0; i < 4 * R; ++i) for (int j = 0; j < 16; ++j) s += c[i][j];
+  for (int i = 0; i < 8; ++i) s += (float)a0[i][0];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // Milliseconds of one launch after a short warm-up launch.
 template <typename F>
 static int timed(F launch, hipEvent_t e0, hipEvent_t e1, float* ms) {
@@ -162,8 +277,24 @@ int main() {
       it = 10000;
       if (timed([&](bool w) { hipLaunchKernelGGL(k_mix, dim3(nb), dim3(256), 0, 0, out, w ? 100 : it, nexp); }, e0, e1, &ms)) return 1;
       double fl2 = (double)nb * 4 * it * 4 * 32768.0;
-      printf("| mfma + %d exp steps per 4 MFMAs | %d | %.1f TFLOP/s | %.0f FLOP |\n", 8 * nexp, wpc, fl2 / ms / 1e9, fl2 / (ms * 1e-3) / 256 / clk);
+      printf("| mfma + %d exp steps per 4 MFMAs, compiler order | %d | %.1f TFLOP/s | %.0f FLOP |\n", 8 * nexp, wpc, fl2 / ms / 1e9, fl2 / (ms * 1e-3) / 256 / clk);
     }
+    it = 10000;
+    const double fl8 = (double)nb * 4 * it * 8 * 32768.0;
+    if (timed([&](bool w) { hipLaunchKernelGGL(k_mfma8, dim3(nb), dim3(256), 0, 0, out, w ? 100 : it); }, e0, e1, &ms)) return 1;
+    printf("| mfma 32x32x16 bf16, 8 accumulators | %d | %.1f TFLOP/s | %.0f FLOP |\n", wpc, fl8 / ms / 1e9, fl8 / (ms * 1e-3) / 256 / clk);
+#define FA_MIXIL(E, M)                                                                              \
+    if (timed([&](bool w) { hipLaunchKernelGGL((k_mixil<E, M>), dim3(nb), dim3(256), 0, 0, out, w ? 100 : it); }, e0, e1, &ms)) return 1; \
+    printf("| mfma + %d exp steps after each MFMA, sched mask 0x%03x | %d | %.1f TFLOP/s | %.0f FLOP |\n", E, M, wpc, fl8 / ms / 1e9, fl8 / (ms * 1e-3) / 256 / clk);
+    FA_MIXIL(1, 0x002) FA_MIXIL(1, 0x402) FA_MIXIL(2, 0x002) FA_MIXIL(2, 0x402)
+    FA_MIXIL(3, 0x002) FA_MIXIL(3, 0x402) FA_MIXIL(4, 0x402)
+#undef FA_MIXIL
+    const double fl16 = (double)nb * 4 * it * 16 * 32768.0;
+#define FA_LDSMFMA(R, TR)                                                                           \
+    if (timed([&](bool w) { hipLaunchKernelGGL((k_ldsmfma<R, TR>), dim3(nb), dim3(256), 0, 0, out, w ? 100 : it); }, e0, e1, &ms)) return 1; \
+    printf("| mfma, A operand from LDS (%s), %d MFMA per operand | %d | %.1f TFLOP/s | %.0f FLOP |\n", TR ? "2 x ds_read_b64_tr_b16" : "ds_read_b128", R, wpc, R * fl16 / ms / 1e9, R * fl16 / (ms * 1e-3) / 256 / clk);
+    FA_LDSMFMA(1, false) FA_LDSMFMA(2, false) FA_LDSMFMA(1, true) FA_LDSMFMA(2, true)
+#undef FA_LDSMFMA
   }
   CHECK(hipFree(out));
   return 0;
