@@ -97,7 +97,8 @@ FA355_API size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *                      entry are ignored and on return are unspecified.
  * dK and dV are accumulated over query tiles by one workgroup per key tile,
  * dQ over key tiles by one workgroup per query tile (S and dP are computed
- * in both), so all three gradients are deterministic.
+ * in both; a workgroup's two wave groups, when it has two, add their partial
+ * sums in a fixed order), so all three gradients are deterministic.
  */
 FA355_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
