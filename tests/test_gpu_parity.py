@@ -178,6 +178,25 @@ def test_bwd_small(fa, B, H, N, d, causal):
     _check_bwd(fa, B, H, N, d, causal, seed=2000 + N + d)
 
 
+# Lengths one below, at and one above the kernels' tile edges (64 and 128
+# keys or queries, and the 192 / 384 steps of two and three tiles), forward
+# and backward. Every other forward uses scale 0.37 instead of 1/sqrt(d). The
+# backward stays at 1/sqrt(d), the scale its absolute tolerance is stated
+# for: at 0.37 (d = 128) |dQ| reaches about 11, and the kernel's own bf16
+# rounding of dS and of the output (emulated on the CPU) already comes to
+# 0.04-0.07 there.
+EDGE_N = [63, 65, 127, 191, 193, 255, 256, 383, 385]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", EDGE_N)
+def test_fwd_bwd_tile_edges(fa, N, d, causal):
+    scale = 0.37 if EDGE_N.index(N) % 2 else None
+    _check_fwd(fa, 1, 2, N, d, causal, seed=4000 + N + d, scale=scale)
+    _check_bwd(fa, 1, 2, N, d, causal, seed=5000 + N + d)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_causal_unsplit_grid(fa, d):
     # 4 query tiles x 132 heads = 528 > 512: the causal dQ kernel without the
