@@ -37,6 +37,10 @@
 //     tiles crossing the diagonal (or the ragged end) evaluate the mask.
 //     Query tiles are issued heaviest first, and the workgroups of one head
 //     stay on one XCD (consecutive workgroup ids go to different XCDs).
+//
+// Long sequences at d = 128 use a second kernel, fa_fwd_pp_kernel (below):
+// the same arithmetic in 256-row workgroups whose two 4-wave groups alternate
+// MFMA and VALU clusters half a tile apart.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -524,10 +528,321 @@ static hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// d = 128 forward, 256 query rows per workgroup in two groups of 4 waves that
+// alternate MFMA and VALU work ("ping-pong").
+//
+// Each wave owns 32 query rows and runs the same online-softmax recurrence as
+// fa_fwd_kernel, but cut into two clusters per key tile j:
+//   M(j): S^T of tile j+1 (16 MFMAs) and O^T += V_j^T P_j^T (16 MFMAs) -- MFMA
+//         and LDS operand reads only;
+//   V(j): the statistics of tile j+1 (mask, max, reference-max update),
+//         P_{j+1} = exp2(s - m), its row sum and bf16 packing, and this
+//         group's tile copies -- VALU and copies only.
+// Group 1 runs half a tile behind group 0 and every cluster ends at a
+// workgroup barrier, so while one wave of a SIMD is in its MFMA cluster the
+// other (waves i and i+4 share a SIMD) is in its VALU cluster. K and V tiles
+// of 64 keys are double-buffered in LDS (64 KiB, so every operand read keeps
+// an immediate offset); group 1 issues every tile copy, in its VALU
+// clusters, and waits for it at the end of its next MFMA cluster.
+// ---------------------------------------------------------------------------
+struct PingPongCfg {
+  static constexpr int D = 128, BM = 256, THREADS = 512, BN = 64, RB = 256;
+  static constexpr int TILE = BN * RB;           // 16 KiB
+  static constexpr int LOADS = TILE / 1024 / 4;  // 1 KiB copies per wave of a group (4)
+  static constexpr int NB = 2, DB = 4, KS = 8;
+};
+
+
+template <bool CAUSAL, bool POS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_pp_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, int BH, int N, int ntq, float c2, int xcd_group) {
+  using C = PingPongCfg;
+  using FC = FwdCfg<128>;
+  constexpr int D = C::D, RB = C::RB, BN = C::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t kl0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kl1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vl0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vl1[C::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wall = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wall >> 2;            // 0: waves 0-3, 1: waves 4-7 (wave i and i+4 share a SIMD)
+  const int w = wall & 3;               // wave within the group
+  const int blk = 2 * w + grp;          // this wave's 32-row block of the 256 rows
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  int head, rank;
+  {
+    const int b = blockIdx.x;
+    if (xcd_group > 0) {
+      const int x = b & 7, s = b >> 3;
+      head = x * xcd_group + s % xcd_group;
+      rank = s / xcd_group;
+    } else {
+      head = b % BH;
+      rank = b / BH;
+    }
+  }
+  const int qt = CAUSAL ? (ntq - 1 - rank) : rank;
+  const int q0 = qt * C::BM;
+  const int qw = q0 + 32 * blk;
+  const int qrow = qw + l32;
+  const size_t off = (size_t)head * N * D;
+  const uint16_t* Kh = K + off;
+  const uint16_t* Vh = V + off;
+
+  const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
+  const int nt = (kend + BN - 1) / BN;
+  const int ntw = CAUSAL ? min(nt, (min(N, qw + 32) + BN - 1) / BN) : nt;
+
+  static_assert(FC::LOADS == C::LOADS, "copy layout shared with fa_fwd_kernel");
+  // This group's 4 waves copy tile t (tiles past the last repeat it: in
+  // bounds, unused) of K (IS_V false) or V into dst, in the layout of
+  // fa_fwd_kernel's copies (rows past N read row N-1). The per-lane offsets
+  // are formed here, in the VALU cluster, rather than held in registers.
+  auto copy_tile = [&](auto is_v, uint8_t* dst, int t) __attribute__((always_inline)) {
+    constexpr bool IS_V = decltype(is_v)::value;
+    const int kb0 = min(t, nt - 1) * BN;
+    const int rmax = N - 1 - kb0;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int r = dma_row<128, IS_V>(w, i, lane);
+      const uint32_t o = (uint32_t)(min(r, rmax) * D + dma_col<128, IS_V>(r, lane)) * 2u;
+      lds_copy16((IS_V ? Vh : Kh) + (size_t)kb0 * D, o,
+                 lds_addr_of(dst + (w * C::LOADS + i) * 1024));
+    }
+  };
+  using KT = std::integral_constant<bool, false>;
+  using VT = std::integral_constant<bool, true>;
+
+  bf16x8 qreg[C::KS];
+  {
+    const uint16_t* qp = Q + off + (size_t)min(qrow, N - 1) * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(qp + ks * 16));
+  }
+  // Prologue copies: K_0 and K_1 (group 0), V_0 and V_1 (group 1).
+  if (grp == 0) {
+    copy_tile(KT{}, kl0, 0);
+    copy_tile(KT{}, kl1, 1);
+  } else {
+    copy_tile(VT{}, vl0, 0);
+    copy_tile(VT{}, vl1, 1);
+  }
+
+  int koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = k_off<D>(l32, 2 * ks + hi);
+  int voff[C::DB];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+      voff[db] = v_off<D>(4 * hi + (sl >> 2), 32 * db + 16 * (g & 1) + 4 * (sl & 3));
+  }
+
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) oacc[i] = zero16();
+  f32x16 sacc[C::NB];
+  bf16x8 pk[BN / 16];
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto scores = [&](const uint8_t* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < C::NB; ++kb) sacc[kb] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * RB + koff[ks]);
+        sacc[kb] = mfma_32x32x16(a, qreg[ks], sacc[kb]);
+      }
+  };
+  auto pv = [&](const uint8_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < BN / 16; ++t)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const uint8_t* vp = vt + 16 * t * RB + voff[db];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)vp);
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp + 8 * RB));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = mfma_32x32x16(a, pk[t], oacc[db]);
+      }
+  };
+  // Statistics of tile kbase (as in fa_fwd_kernel), then P = exp2(s - m) for
+  // it, its row sum and bf16 packing into the next PV operands.
+  auto softmax = [&](int kbase) __attribute__((always_inline)) {
+    const bool masked = (CAUSAL && kbase + BN - 1 > qw) || (kbase + BN > N);
+    if (masked) {
+#pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          const bool ok = key < N && (!CAUSAL || key <= qrow);
+          if constexpr (POS) sacc[kb][i] = ok ? sacc[kb][i] : -INFINITY;
+          else sacc[kb][i] = ok ? sacc[kb][i] * c2 : -INFINITY;
+        }
+    } else if constexpr (!POS) {
+#pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] *= c2;
+    }
+    float tmax = tile_max<C::NB>(sacc);
+    if constexpr (POS) tmax *= c2;
+    tmax = halves_max(tmax);
+    const bool grow = tmax > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < C::NB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (POS) sacc[kb][i] = fast_exp2(fmaf(sacc[kb][i], c2, -m_use));
+        else sacc[kb][i] = fast_exp2(sacc[kb][i] - m_use);
+      }
+    l_run += tile_sum<C::NB>(sacc);
+#pragma unroll
+    for (int t = 0; t < BN / 16; ++t) {
+      const f32x16& p = sacc[t >> 1];
+      const int r0 = (t & 1) * 8;
+      pk[t] = pack_bf16x8(p[r0 + 0], p[r0 + 1], p[r0 + 2], p[r0 + 3],
+                          p[r0 + 4], p[r0 + 5], p[r0 + 6], p[r0 + 7]);
+    }
+  };
+
+  // MFMA cluster of tile j: scores of tile j+1 from k_next (computed on the
+  // wave's last tile too, from whatever the buffer holds, never used: one
+  // code path) and O += V_j P_j; then the wait for this wave's copies of the
+  // previous VALU cluster (only group 1 copies).
+  auto mcluster = [&](int j, const uint8_t* k_next, const uint8_t* v_this) __attribute__((always_inline)) {
+    if (j < ntw) {
+      scores(k_next);
+      pv(v_this);
+      constexpr int kMfma = 0x008, kDsRead = 0x100;
+      // Operand reads run a few MFMAs ahead: one K read per score MFMA,
+      // then two transposing V reads per PV MFMA.
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * C::KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4 * C::DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+      }
+    }
+    wait_dma();
+  };
+
+  wait_dma();
+  __syncthreads();
+  // Prologue: every wave forms P_0 from K_0.
+  scores(kl0);
+  softmax(0);
+  __syncthreads();
+  // Group 1 starts one cluster later: its first slot copies K_2 into K_0's
+  // buffer (free now) and waits for it; group 0 meanwhile runs M(0).
+  if (grp == 1) {
+    copy_tile(KT{}, kl0, 2);
+    wait_dma();
+    __syncthreads();
+  }
+
+  // Every wave runs the same clusters: M(j), barrier, V(j), barrier. With
+  // group 1 one barrier behind, one wave of each SIMD is in an MFMA cluster
+  // while the other is in a VALU cluster. V(j) is the softmax of tile j+1
+  // and, for group 1, the copies of K_{j+3} (into K_{j+1}'s buffer) and
+  // V_{j+2} (into V_j's), both last read by M(j) of the two groups.
+  auto step = [&](auto ph, int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(ph)::value;   // j % 2
+    const uint8_t* const k_next = P ? kl0 : kl1;   // K_{j+1}
+    const uint8_t* const v_this = P ? vl1 : vl0;   // V_j
+    uint8_t* const k_fill = P ? kl0 : kl1;         // K_{j+1}'s buffer, gets K_{j+3}
+    uint8_t* const v_fill = P ? vl1 : vl0;         // V_j's buffer, gets V_{j+2}
+    mcluster(j, k_next, v_this);
+    __syncthreads();
+    if (j + 1 < ntw) softmax((j + 1) * BN);
+    if (grp == 1) {
+      copy_tile(KT{}, k_fill, j + 3);
+      copy_tile(VT{}, v_fill, j + 2);
+    }
+    __syncthreads();
+  };
+  for (int j = 0; j < nt; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
+  }
+  if (grp == 0) __syncthreads();
+  wait_dma();
+
+  const float l_tot = halves_sum(l_run);
+  if (qrow < N) {
+    const float inv = 1.f / l_tot;
+    uint16_t* orow = O + off + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * hi;
+        u32x2 pr = {pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                    pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d0) = pr;
+      }
+    if (hi == 0) LSE[(size_t)head * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+template <bool CAUSAL, bool POS>
+static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                uint16_t* o, float* lse, int BH, int N, float scale,
+                                hipStream_t stream) {
+  const int ntq = (N + PingPongCfg::BM - 1) / PingPongCfg::BM;
+  const int xcd_group = (BH % 8 == 0) ? BH / 8 : 0;
+  const float c2 = scale * kLog2e;
+  dim3 grid((unsigned)(ntq * BH)), block(PingPongCfg::THREADS);
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<CAUSAL, POS>), grid, block, 0, stream,
+                     q, k, v, o, lse, BH, N, ntq, c2, xcd_group);
+  return hipGetLastError();
+}
+
 hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* o, float* lse, int BH, int N, int d, float scale,
                         bool causal, hipStream_t stream) {
   const bool pos = scale > 0.f;
+  // Long d = 128 sequences (on average at least ~64 key tiles per query
+  // tile) with at least one 256-row workgroup per CU take the two-group
+  // kernel: measured 3-5 % faster there (B=1, H=16, N=16384 causal; N=8192
+  // causal and not; B=2, H=32, N=4096 non-causal), but 5-14 % slower on
+  // shorter causal sequences (N = 4096, 2048), where its 256-row workgroups
+  // leave SIMDs idle across a 4-tile diagonal that a second, independent
+  // workgroup would fill.
+  if (d == 128 && (long)((N + PingPongCfg::BM - 1) / PingPongCfg::BM) * BH >= 256 &&
+      N >= (causal ? 8192 : 4096)) {
+    if (causal && pos) return launch_fwd_pp<true, true>(q, k, v, o, lse, BH, N, scale, stream);
+    if (!causal && pos) return launch_fwd_pp<false, true>(q, k, v, o, lse, BH, N, scale, stream);
+    if (causal && !pos) return launch_fwd_pp<true, false>(q, k, v, o, lse, BH, N, scale, stream);
+    return launch_fwd_pp<false, false>(q, k, v, o, lse, BH, N, scale, stream);
+  }
 #define FA_FWD_CASE(DD, CC, PP) \
   if (d == DD && causal == CC && pos == PP) \
     return launch_fwd<DD, CC, PP>(q, k, v, o, lse, BH, N, scale, stream);

@@ -277,6 +277,36 @@ def test_workload5_fwd_bwd(fa):
                 assert_close(f"{name}[{b},{h}]", got[b, h], ref, TOL_GRAD)
 
 
+# ---------------------------------------------------------------- two-group forward
+def _check_fwd_sampled(fa, B, H, N, d, causal, seed, heads, scale=None):
+    print(f"[fwd sampled] B={B} H={H} N={N} d={d} causal={causal} scale={scale} heads={heads}",
+          flush=True)
+    shape = (B, H, N, d)
+    qb, kb, vb = (fi.random_bf16(shape, seed + i) for i in range(3))
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    o, lse, _ = _run_fwd(fa, qb, kb, vb, scale, causal)
+    o_np, l_np = from_gpu(o), from_gpu(lse)
+    for h in heads:
+        ro, rl = oracle.attention_fwd(bits_to_f64(qb[0, h]), bits_to_f64(kb[0, h]),
+                                      bits_to_f64(vb[0, h]), scale, causal)
+        assert_close(f"O[0,{h}]", o_np[0, h], ro, TOL_O)
+        assert_close(f"LSE[0,{h}]", l_np[0, h], rl, TOL_LSE)
+
+
+# Long d = 128 grids take the two-group (256-row, alternating MFMA / VALU
+# cluster) kernel: non-causal N >= 4096 and causal N >= 8192 with at least
+# 256 of its workgroups. Ragged lengths (the last 256-row and 64-key tiles
+# partial), a negative and a zero scale; every row of sampled heads.
+@pytest.mark.parametrize("N,H,causal,scale,heads", [
+    (4100, 64, False, None, [0, 37, 63]),
+    (8200, 32, True, None, [0, 31]),
+    (4096, 64, False, -0.21, [5]),
+    (8192, 32, True, 0.0, [9]),
+])
+def test_fwd_two_group_kernel(fa, N, H, causal, scale, heads):
+    _check_fwd_sampled(fa, 1, H, N, 128, causal, seed=6000 + N, heads=heads, scale=scale)
+
+
 # ---------------------------------------------------------------- long context
 @pytest.mark.parametrize("N,H,d", [(65536, 2, 128), (100003, 1, 64)])
 def test_fwd_long_context_sampled_rows(fa, N, H, d):
