@@ -113,7 +113,8 @@ def long_forwards(fa, torch, fi, dev, warmup=20, calls=50):
         ms = [e[0].elapsed_time(e[1]) for e in ev]
         avg = sum(ms) / len(ms)
         tf = w.fwd_flops() / (avg * 1e-3) / 1e12
-        out.append({"workload": w.name, "avg_ms": round(avg, 4),
+        out.append({"workload": w.name, "kernel": fa.fa_fwd_kernel_name(w.B, w.H, w.N, w.d, w.causal),
+                    "avg_ms": round(avg, 4),
                     "median_ms": round(median(ms), 4), "min_ms": round(min(ms), 4),
                     "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                     "target_frac": 0.5})
@@ -330,7 +331,8 @@ def main():
                "achieved": bwd_tf, "avg_ms": b_avg,
                "traffic": recorded_traffic(args.workload, "fa_bwd")}
     else:
-        dom = {"launch": "fa_fwd (kernel fa_fwd_kernel)", "achieved": fwd_tf, "avg_ms": f_avg,
+        kname = fa.fa_fwd_kernel_name(w.B, w.H, w.N, w.d, w.causal)
+        dom = {"launch": f"fa_fwd (kernel {kname})", "achieved": fwd_tf, "avg_ms": f_avg,
                "traffic": recorded_traffic(args.workload, "fa_fwd")}
     roofline = {"bound": "mfma", "achieved": round(dom["achieved"], 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

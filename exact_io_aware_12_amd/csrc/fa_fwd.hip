@@ -825,19 +825,22 @@ static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint
   return hipGetLastError();
 }
 
+// Long d = 128 sequences (on average at least ~64 key tiles per query tile)
+// with at least one 256-row workgroup per CU take the two-group kernel:
+// measured 3-5 % faster there (B=1, H=16, N=16384 causal; N=8192 causal and
+// not; B=2, H=32, N=4096 non-causal), but 5-14 % slower on shorter causal
+// sequences (N = 4096, 2048), where its 256-row workgroups leave SIMDs idle
+// across a 4-tile diagonal that a second, independent workgroup would fill.
+bool fwd_uses_two_group_kernel(int BH, int N, int d, bool causal) {
+  return d == 128 && (long)((N + PingPongCfg::BM - 1) / PingPongCfg::BM) * BH >= 256 &&
+         N >= (causal ? 8192 : 4096);
+}
+
 hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* o, float* lse, int BH, int N, int d, float scale,
                         bool causal, hipStream_t stream) {
   const bool pos = scale > 0.f;
-  // Long d = 128 sequences (on average at least ~64 key tiles per query
-  // tile) with at least one 256-row workgroup per CU take the two-group
-  // kernel: measured 3-5 % faster there (B=1, H=16, N=16384 causal; N=8192
-  // causal and not; B=2, H=32, N=4096 non-causal), but 5-14 % slower on
-  // shorter causal sequences (N = 4096, 2048), where its 256-row workgroups
-  // leave SIMDs idle across a 4-tile diagonal that a second, independent
-  // workgroup would fill.
-  if (d == 128 && (long)((N + PingPongCfg::BM - 1) / PingPongCfg::BM) * BH >= 256 &&
-      N >= (causal ? 8192 : 4096)) {
+  if (fwd_uses_two_group_kernel(BH, N, d, causal)) {
     if (causal && pos) return launch_fwd_pp<true, true>(q, k, v, o, lse, BH, N, scale, stream);
     if (!causal && pos) return launch_fwd_pp<false, true>(q, k, v, o, lse, BH, N, scale, stream);
     if (causal && !pos) return launch_fwd_pp<true, false>(q, k, v, o, lse, BH, N, scale, stream);

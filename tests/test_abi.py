@@ -34,8 +34,21 @@ def fa():
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_fwd",
                            "fa_decode_workspace_bytes", "fa_fa1_fwd", "fa_fa1_workspace_bytes",
-                           "fa_fwd", "fa_strerror", "fa_unfused_fwd",
+                           "fa_fwd", "fa_fwd_kernel_name", "fa_strerror", "fa_unfused_fwd",
                            "fa_unfused_workspace_bytes"]
+
+
+def test_fwd_kernel_name_follows_the_dispatch_rule(fa):
+    # Two-group kernel: d = 128, causal N >= 8192 or non-causal N >= 4096, and
+    # at least 256 of its 256-row workgroups; otherwise the 128-row kernel.
+    assert fa.fa_fwd_kernel_name(1, 16, 16384, 128, True) == "fa_fwd_pp_kernel"
+    assert fa.fa_fwd_kernel_name(2, 32, 4096, 128, True) == "fa_fwd_kernel"
+    assert fa.fa_fwd_kernel_name(2, 32, 4096, 128, False) == "fa_fwd_pp_kernel"
+    assert fa.fa_fwd_kernel_name(2, 16, 2048, 128, True) == "fa_fwd_kernel"
+    assert fa.fa_fwd_kernel_name(1, 1, 16384, 128, True) == "fa_fwd_kernel"      # 64 workgroups
+    assert fa.fa_fwd_kernel_name(1, 16, 16384, 64, True) == "fa_fwd_kernel"      # d = 64
+    assert fa.fa_fwd_kernel_name(0, 16, 16384, 128, True) is None
+    assert fa.fa_fwd_kernel_name(1, 16, 16384, 96, True) is None
 
 
 def test_every_declared_symbol_is_exported():
