@@ -20,7 +20,10 @@
 //   2. fa_bwd_dkdv:  dK and dV. One workgroup per key tile pair (8 wave64s,
 //      two per SIMD: 4 key blocks of 32 x 2 query halves); the loop runs over
 //      64-query tiles (outer loop over K/V, inner over Q, so dK and dV stay
-//      in registers).
+//      in registers). The two query halves are two groups of 4 waves that
+//      take turns, one barrier apart: while one wave of a SIMD runs its MFMA
+//      cluster (dV, dK of the previous query tile, then S, dP of this one),
+//      the other runs its VALU cluster (P and dS of its current tile).
 // Splitting dQ from dK/dV costs two extra matmuls per tile pair (S and dP are
 // computed in both kernels: 7 instead of 5), and buys the removal of every
 // cross-workgroup accumulation: on this multi-XCD device, device-scope fp32
@@ -33,19 +36,24 @@
 //     staged in LDS once per key tile), so P and dS sit in registers in
 //     exactly the layout the B operand of dV^T += dO^T P and
 //     dK^T += Q^T dS needs (k-slots are queries). Q and dO tiles go from
-//     HBM/L2 straight into LDS (global_load_lds_dwordx4, double-buffered) in
+//     HBM/L2 straight into LDS (global_load_lds_dwordx4, a ring of three) in
 //     one XOR swizzle that serves both the row-major operand reads of S and
 //     dP (ds_read_b128) and the transposing reads that give Q^T and dO^T
-//     (ds_read_b64_tr_b16) without bank conflicts.
+//     (ds_read_b64_tr_b16) without bank conflicts. Each lane loads one
+//     row's LSE and D; DPP row broadcasts hand every accumulator element its
+//     row's values.
 //   * dQ kernel: the transposed form of the forward pass, one query per lane:
 //     S^T = K Q^T and dP^T = V dO^T (Q and dO rows in registers as B
 //     operands, K and V rows from LDS), P^T and dS^T element-wise with the
 //     lane's own LSE and D, and dQ^T += K^T dS^T with dS^T fed from the
 //     accumulator registers as the B operand and K^T from transposing reads
 //     of the same swizzled K tile.
-//   * Scheduling-group barriers interleave the MFMAs with the VALU work and
-//     the LDS operand reads of each phase.
+//   * dQ kernel: scheduling-group barriers interleave the MFMAs with the VALU
+//     work and the LDS operand reads of each phase. dK/dV kernel: its MFMA
+//     cluster is an explicit software pipeline (operands read a fixed number
+//     of MFMAs ahead, the order pinned by scheduling barriers).
 #include <type_traits>
+#include <utility>
 
 #include "fa_common.h"
 
@@ -69,8 +77,12 @@ struct BwdCfg {
   static constexpr int VLOADS = VTILE / 1024 / WAVES;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  // The pair's partial dK (then dV) sums go through the Q / dO buffers.
-  static_assert(4 * 16 * DB * 64 * 4 <= 4 * QTILE, "partial sums fit the Q/dO buffers");
+  static constexpr int PREFETCH = 4;       // MFMAs whose LDS operands are in flight
+  // A ring of three Q and three dO tiles plus one K and one V key tile: the
+  // whole 160 KiB of a CU's LDS at d = 128.
+  static_assert(6 * QTILE + 2 * VTILE <= 160 * 1024, "LDS");
+  // The partial dK (then dV) sums of group 1 go through the Q / dO buffers.
+  static_assert(4 * 16 * DB * 64 * 4 <= 6 * QTILE, "partial sums fit the Q/dO buffers");
 };
 
 // Swizzled byte offset of 2-byte element (row, col) in a tile with R-byte
@@ -104,10 +116,6 @@ __device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(lds_addr) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_copy4(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(lds_addr) : "memory", "m0");
-}
 // Scalar-base form: the tile's base address is one SGPR pair and each lane
 // adds a 32-bit byte offset (no per-lane 64-bit address arithmetic).
 __device__ __forceinline__ void lds_copy16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
@@ -137,14 +145,6 @@ __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, const
   }
 }
 
-// Per-row statistics of one query tile into LDS (64 fp32 LSE, then 64 fp32
-// D; rows past N read row N-1): one 4-byte copy per lane of one wave.
-__device__ __forceinline__ void dma_stats(const float* __restrict__ lse, const float* __restrict__ dv,
-                                          const float* lds, int q0, int N, int lane) {
-  lds_copy4(lse + min(q0 + lane, N - 1), lds_addr(lds));
-  lds_copy4(dv + min(q0 + lane, N - 1), lds_addr(lds + 64));
-}
-
 __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // s_waitcnt vmcnt(0)
 }
@@ -159,6 +159,33 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* base, int o0, int o1
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// DPP row broadcast: every lane receives the value of lane I of its 16-lane
+// row (row_newbcast).
+template <int I>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + I, 0xF, 0xF, true));
+}
+// f(integral_constant<int, I>) for each I of the sequence, in order.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// dK, dV for one key tile (or a causal pair of them) per workgroup. The two
+// query halves of each 64-query tile are two groups of 4 waves (group g =
+// waves 4g .. 4g+3; waves w and w+4 share a SIMD) that alternate two
+// clusters per query tile s:
+//   M(s): dV^T += dO_{s-1}^T P_{s-1} and dK^T += Q_{s-1}^T dS_{s-1} (4*DB
+//         MFMAs, from the packed P / dS of the previous tile), then S and dP
+//         of tile s (2*KS MFMAs): MFMAs and LDS operand reads only;
+//   V(s): P = exp2(S*scale*log2e - LSE*log2e) and dS = P o (dP - D) of tile s,
+//         packed to bf16: VALU work only.
+// Group 1 runs one workgroup barrier behind group 0, so while one wave of a
+// SIMD issues MFMAs the other issues VALU work. Q / dO tiles live in a ring
+// of three LDS buffers: in V(s), after both groups' M(s) have read tile s-1,
+// group 1 copies tile s+2 into its buffers, and it waits for the copies at
+// the end of its M(s+1), before the barrier that lets group 0 read them.
+// The two groups' partial dK / dV are summed in LDS at the end of a key tile.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -168,20 +195,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int BH, int N, int nunits, float c2, float scale, int xcd_group) {
   using C = BwdCfg<D>;
   constexpr int KS = C::KS, DB = C::DB, RB = C::RB;
-  // Q tiles (buffers 0, 1) then dO tiles (buffers 2, 3); at the end of a key
-  // tile the same bytes carry the partial dK / dV sums.
-  __shared__ __attribute__((aligned(1024))) uint8_t qo_lds[4 * C::QTILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[C::VTILE];      // this key tile's K
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[C::VTILE];      // and V
-  __shared__ __attribute__((aligned(256))) float st_lds[2][2 * C::BMQ];    // LSE, D
+  constexpr int GLOADS = C::QTILE / 1024 / 4;   // 1 KiB copies per wave of group 1, per tile
+  // Q tiles in buffers 0-2, dO tiles in 3-5 (a ring of three query tiles),
+  // this key tile's K and V; at the end of a key tile the first bytes of the
+  // ring carry the partial dK / dV sums.
+  __shared__ __attribute__((aligned(1024))) uint8_t qo_lds[6 * C::QTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[C::VTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[C::VTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   // Wave w: keys 32*kb .. +31 of the key tile, queries 32*qh .. +31 of each
-  // query tile. The two waves of a key block (qh = 0, 1) share a SIMD with
-  // waves of other key blocks, and their partial dK / dV are summed at the end.
+  // query tile; qh is the wave's group. Waves w and w+4 share a SIMD.
   const int kb = w & 3, qh = w >> 2;
 
   // Workgroup -> (head, work unit). Causal: unit u covers the key tiles u and
@@ -212,48 +239,62 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float* Dh = Dvec + (size_t)head * N;
   const int nqt = (N + C::BMQ - 1) / C::BMQ;
 
-  // Transposing-read lane offsets: lane (group g = lane/16, source s = lane%16)
-  // points at row 4*hi + s/4 (plus 16t + 8*half) and column 16*(g&1) + 4*(s&3)
-  // (plus 32*block) of a row-major tile.
+  // Per-lane LDS byte offsets, k-step / block 0. The swizzle only moves
+  // 16-byte chunks within a row, so the other k-steps and 32-column blocks
+  // are XORs of these (k-step ks: ^ ks << 5 for row-major reads; block db:
+  // ^ db << 6 for transposing reads, and the half 8 rows on: ^ 32, + 8 rows),
+  // one register each instead of one per (k-step, block, half).
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  // Per-lane LDS offsets. The swizzles only look at bits 0-3 of the row, so
-  // whole 16-row (and 32-row) steps are plain immediate offsets: one register
-  // per (half, 32-column block) for transposing reads, one per k-step for
-  // the row-major operand reads (Q, dO, K and V rows alike).
-  int tq_off[2][DB];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) tq_off[h][db] = sw_off<RB>(tr_row + 8 * h, 32 * db + tr_col);
-  int rq_off[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) rq_off[ks] = sw_off<RB>(l32, 16 * ks + 8 * hi);
+  const int rq0 = sw_off<RB>(l32, 8 * hi);
+  const int tq0 = sw_off<RB>(tr_row, tr_col);
 
   f32x16 dkacc[DB], dvacc[DB];
-  int k0 = 0, kk = 0;                 // first key of the tile, this lane's key
+  f32x16 sacc, pacc;        // S and dP of the current query tile (this wave's 32 x 32)
+  bf16x8 pbv[2], sbv[2];    // packed P and dS of the previous query tile
 
   const int nkt_ = (N + C::BNK - 1) / C::BNK;
   const int nparts = (CAUSAL && 2 * unit + 1 != nkt_) ? 2 : 1;
   for (int part = 0; part < nparts; ++part) {
     const int kt = part == 0 ? unit : nkt_ - 1 - unit;
-    k0 = kt * C::BNK;
-    kk = k0 + 32 * kb + l32;
-    // Query tiles it_lo .. nqt-1 (causal: from the one holding key k0), in
-    // descending order in the first part of a causal unit.
+    const int k0 = kt * C::BNK;
+    const int kk = k0 + 32 * kb + l32;
     const bool rev = CAUSAL && part == 0;
     const int it_lo = CAUSAL ? (k0 / C::BMQ) : 0;
     const int nsteps = nqt - it_lo;
     auto tile_at = [&](int step) __attribute__((always_inline)) {
       return rev ? nqt - 1 - step : it_lo + step;
     };
+    auto qbuf = [&](int b) __attribute__((always_inline)) { return qo_lds + b * C::QTILE; };
+    auto obuf = [&](int b) __attribute__((always_inline)) { return qo_lds + (3 + b) * C::QTILE; };
+    // Group 1's copy of query tile `step` (Q and dO) into buffer b: wave kb
+    // copies rows 16kb .. 16kb+15 (GLOADS KiB); tiles past the last repeat
+    // it (in bounds, unused), rows past N read row N-1.
+    auto copy_tile = [&](int step, int b) __attribute__((always_inline)) {
+      const int row0 = tile_at(min(step, nsteps - 1)) * C::BMQ;
+      constexpr int RPL = 1024 / RB, CPR = RB / 16;
+      const bool full = row0 + C::BMQ <= N;
+#pragma unroll
+      for (int i = 0; i < GLOADS; ++i) {
+        const int lrow = (kb * GLOADS + i) * RPL;
+        const int row = lrow + lane / CPR;
+        const int c = (lane % CPR) ^ sw_xor<RB>(row);
+        const int src_row = full ? row0 + row : min(row0 + row, N - 1);
+        const uint32_t voff = (uint32_t)(src_row * RB + c * 16);
+        lds_copy16s(Qh, voff, lds_addr(qbuf(b) + lrow * RB));
+        lds_copy16s(dOh, voff, lds_addr(obuf(b) + lrow * RB));
+      }
+    };
 
-    // Copies: this key tile's K and V, the first query tile.
+    // Prologue: this key tile's K and V, query tiles 0 and 1 (all waves).
     dma_rows<D, C::VLOADS>(K + off, k_lds, k0, N, w, lane);
     dma_rows<D, C::VLOADS>(V + off, v_lds, k0, N, w, lane);
-    dma_rows<D, C::QLOADS>(Qh, qo_lds, tile_at(0) * C::BMQ, N, w, lane);
-    dma_rows<D, C::QLOADS>(dOh, qo_lds + 2 * C::QTILE, tile_at(0) * C::BMQ, N, w, lane);
-    if (w == 0) dma_stats(LSEh, Dh, st_lds[0], tile_at(0) * C::BMQ, N, lane);
+    dma_rows<D, C::QLOADS>(Qh, qbuf(0), tile_at(0) * C::BMQ, N, w, lane);
+    dma_rows<D, C::QLOADS>(dOh, obuf(0), tile_at(0) * C::BMQ, N, w, lane);
+    if (nsteps > 1) {
+      dma_rows<D, C::QLOADS>(Qh, qbuf(1), tile_at(1) * C::BMQ, N, w, lane);
+      dma_rows<D, C::QLOADS>(dOh, obuf(1), tile_at(1) * C::BMQ, N, w, lane);
+    }
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
       dkacc[i] = zero16();
@@ -262,106 +303,179 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vmem();
     __syncthreads();
 
-    const uint8_t* krows = k_lds + 32 * kb * RB;   // this wave's 32 K rows
-    const uint8_t* vrows = v_lds + 32 * kb * RB;   // and V rows
-    for (int step = 0; step < nsteps; ++step) {
-      // Buffers of this query tile (b) and of the next one (b ^ 1); this
-      // wave's 32 queries start 32*qh rows into the tile.
-      const int b = step & 1;
-      const uint8_t* qt = qo_lds + b * C::QTILE + 32 * qh * RB;
-      const uint8_t* ot = qo_lds + (2 + b) * C::QTILE + 32 * qh * RB;
-      const float* st = st_lds[b] + 32 * qh;
-      const int qbase = tile_at(step) * C::BMQ;
-      const int qw = qbase + 32 * qh;            // first query of this wave
-      if (step + 1 < nsteps) {
-        const int qn = tile_at(step + 1) * C::BMQ;
-        dma_rows<D, C::QLOADS>(Qh, qo_lds + (b ^ 1) * C::QTILE, qn, N, w, lane);
-        dma_rows<D, C::QLOADS>(dOh, qo_lds + (2 + (b ^ 1)) * C::QTILE, qn, N, w, lane);
-        if (w == 0) dma_stats(LSEh, Dh, st_lds[b ^ 1], qn, N, lane);
-      }
-      // ---- S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-      // (one key per lane: K and V rows from LDS as B operands).
-      f32x16 sacc = zero16(), pacc = zero16();
+    // S = Q K^T and dP = dO V^T for this wave's 32 queries of the tile in
+    // buffer b x its 32 keys. aq / ak: row-major read offsets of this wave's
+    // query rows in buffer b / of its key rows, k-step 0.
+    auto sdp = [&](int aq, int ak) __attribute__((always_inline)) {
+      sacc = zero16();
+      pacc = zero16();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + rq_off[ks]);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(ot + rq_off[ks]);
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(krows + rq_off[ks]);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vrows + rq_off[ks]);
-        sacc = mfma_32x32x16(aq, bk, sacc);
-        pacc = mfma_32x32x16(ad, bv, pacc);
+        const int oq = aq ^ (ks << 5), ok = ak ^ (ks << 5);
+        const bf16x8 a_q = *reinterpret_cast<const bf16x8*>(qbuf(0) + oq);
+        const bf16x8 a_o = *reinterpret_cast<const bf16x8*>(obuf(0) + oq);
+        const bf16x8 b_k = *reinterpret_cast<const bf16x8*>(k_lds + ok);
+        const bf16x8 b_v = *reinterpret_cast<const bf16x8*>(v_lds + ok);
+        sacc = mfma_32x32x16(a_q, b_k, sacc);
+        pacc = mfma_32x32x16(a_o, b_v, pacc);
       }
-      // ---- x = S*scale*log2e - LSE*log2e, -inf where masked (a small branch
-      // taken only on tiles that cross the diagonal or N), P = exp2(x),
-      // dS = P o (dP - D), packed to bf16 per 16-query group t (registers
-      // 8t .. 8t+7: the k-slot order of the dV / dK B operands).
+    };
+    // -LSE*log2(e) and D of this wave's rows of tile `step`, one row per
+    // lane: lane l holds row 8*((l%16)/4) + 4*(l/32) + l%4, which is the row
+    // of accumulator element l%16 in lane l's half of the wave, so element i
+    // takes its value from lane i of its 16-lane row (a DPP broadcast). Rows
+    // past N read row N-1 (their P is zero). Issued at the start of the MFMA
+    // cluster, used in the VALU cluster.
+    float nlse_l, d_l;
+    const int srow = 8 * ((lane & 15) >> 2) + 4 * hi + (lane & 3);
+    auto load_stats = [&](int step) __attribute__((always_inline)) {
+      const int r = min(tile_at(step) * C::BMQ + 32 * qh + srow, N - 1);
+      nlse_l = LSEh[r];
+      d_l = Dh[r];
+    };
+    // P and dS of tile `step` from sacc / pacc, packed (registers 8t .. 8t+7:
+    // the k-slot order of the dV / dK B operands).
+    auto valu = [&](int step) __attribute__((always_inline)) {
+      const int qw = tile_at(step) * C::BMQ + 32 * qh;
+      const float nl = nlse_l * -kLog2e;
+      static_for([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        sacc[i] = fmaf(sacc[i], c2, row_bcast<i>(nl));
+        pacc[i] = pacc[i] - row_bcast<i>(d_l);
+      }, std::make_integer_sequence<int, 16>{});
       const bool masked = (CAUSAL && qw < kk - l32 + 31) || qw + 32 > N || k0 + C::BNK > N;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + 8 * g4 + 4 * hi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sacc[4 * g4 + e] = fmaf(sacc[4 * g4 + e], c2, -lse4[e] * kLog2e);
-      }
       if (masked) {
+        // Element i holds query qw + 4hi + c_i (c_i = 8(i/4) + i%4): masked
+        // when the key is above it (causal), or it or the key is past N.
+        const int qd = kk - qw - 4 * hi, qr = N - qw - 4 * hi;
+        const bool kout = kk >= N;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int q = qw + 8 * (i >> 2) + 4 * hi + (i & 3);
-          sacc[i] = ((CAUSAL && kk > q) || kk >= N || q >= N) ? -INFINITY : sacc[i];
+          const int ci = 8 * (i >> 2) + (i & 3);
+          sacc[i] = ((CAUSAL && qd > ci) || kout || ci >= qr) ? -INFINITY : sacc[i];
         }
       }
-      bf16x8 pbv[2], sbv[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         float pv[8], dv8[8];
 #pragma unroll
         for (int g2 = 0; g2 < 2; ++g2) {
           const int g4 = 2 * t + g2;
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + C::BMQ + 8 * g4 + 4 * hi);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float p = fast_exp2(sacc[4 * g4 + e]);
             pv[4 * g2 + e] = p;
-            dv8[4 * g2 + e] = p * (pacc[4 * g4 + e] - d4[e]);
+            dv8[4 * g2 + e] = p * pacc[4 * g4 + e];
           }
         }
         pbv[t] = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
         sbv[t] = pack_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
       }
-      // ---- dV^T += dO^T P and dK^T += Q^T dS (k-slots = this wave's queries).
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dvacc[db] = mfma_32x32x16(tr_operand(ot + 16 * t * RB, tq_off[0][db], tq_off[1][db]), pbv[t], dvacc[db]);
-          dkacc[db] = mfma_32x32x16(tr_operand(qt + 16 * t * RB, tq_off[0][db], tq_off[1][db]), sbv[t], dkacc[db]);
-        }
-      }
-      {
-        constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
-        // S / dP MFMAs with their operand reads, then the dV / dK MFMAs with
-        // two transposing reads each and the exp / dS / packing work.
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4 * DB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(kValu, 5, 0);
-        }
-      }
+    };
+
+    // Prologue: every wave forms P, dS of tile 0.
+    load_stats(0);
+    sdp(rq0 + 32 * qh * RB, rq0 + 32 * kb * RB);
+    valu(0);
+    __syncthreads();
+    // Group 1 starts one barrier later: its first slot copies tile 2.
+    if (qh == 1) {
+      if (nsteps > 2) copy_tile(2, 2);
       wait_vmem();
       __syncthreads();
     }
 
-    // ---- Sum the pair's partial dK^T, dV^T through LDS (lane-contiguous
+    // Step s (1 .. nsteps): M(s), barrier, V(s), barrier. Tile s sits in
+    // buffer s % 3, tile s-1 in (s-1) % 3, which then receives tile s+2. The
+    // last step (no tile s) only finishes dV, dK of tile s-1.
+    auto step = [&](auto last, int s, int p, int prev) __attribute__((always_inline)) {
+      constexpr bool LAST = decltype(last)::value;
+      // Buffer b's bytes start b * QTILE after buffer 0's (a multiple of 16
+      // KiB, above the bits the XORs touch). The offsets are re-derived in
+      // every step (an empty asm hides that they do not change), so that
+      // three registers stay live across the loop rather than one per
+      // (k-step, operand).
+      int aq = rq0 + 32 * qh * RB, ak = rq0 + 32 * kb * RB, at = tq0 + 32 * qh * RB;
+      asm volatile("" : "+v"(aq), "+v"(ak), "+v"(at));
+      if constexpr (!LAST) load_stats(s);
+      // The MFMA cluster as an explicit software pipeline: MFMAs 0 .. 4*DB-1
+      // are dV^T / dK^T of tile s-1 (A: transposing reads of dO / Q, B: the
+      // packed P / dS), then, unless this is the last step, S and dP of tile
+      // s in k-step pairs (A: Q / dO rows, B: K / V rows). The operands of
+      // MFMA i + PREFETCH are read before MFMA i is issued, and scheduling
+      // barriers keep that order (left to itself, the scheduler may spend
+      // the look-ahead on reads needed much later).
+      constexpr int NM = 4 * DB + (LAST ? 0 : 2 * KS);
+      const int atb = at + prev * C::QTILE, aqb = aq + p * C::QTILE;
+      bf16x8 opa[C::PREFETCH + 1], opb[C::PREFETCH + 1];
+      auto fetch = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int r = i % (C::PREFETCH + 1);
+        if constexpr (i < 4 * DB) {
+          constexpr int t = i / (2 * DB), db = (i / 2) % DB, isk = i % 2;
+          const int o0 = atb ^ (db << 6), o1 = (o0 ^ 32) + 8 * RB;
+          opa[r] = tr_operand((isk ? qbuf(0) : obuf(0)) + 16 * t * RB, o0, o1);
+        } else {
+          constexpr int j = i - 4 * DB, ks = j / 2, isp = j % 2;
+          const int oq = aqb ^ (ks << 5), ok = ak ^ (ks << 5);
+          opa[r] = *reinterpret_cast<const bf16x8*>((isp ? obuf(0) : qbuf(0)) + oq);
+          opb[r] = *reinterpret_cast<const bf16x8*>((isp ? v_lds : k_lds) + ok);
+        }
+      };
+      auto mfma_i = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int r = i % (C::PREFETCH + 1);
+        if constexpr (i < 4 * DB) {
+          constexpr int t = i / (2 * DB), db = (i / 2) % DB, isk = i % 2;
+          if constexpr (isk) dkacc[db] = mfma_32x32x16(opa[r], sbv[t], dkacc[db]);
+          else dvacc[db] = mfma_32x32x16(opa[r], pbv[t], dvacc[db]);
+        } else {
+          constexpr int j = i - 4 * DB, isp = j % 2;
+          if constexpr (j < 2) {
+            if constexpr (isp) pacc = mfma_32x32x16(opa[r], opb[r], zero16());
+            else sacc = mfma_32x32x16(opa[r], opb[r], zero16());
+          } else {
+            if constexpr (isp) pacc = mfma_32x32x16(opa[r], opb[r], pacc);
+            else sacc = mfma_32x32x16(opa[r], opb[r], sacc);
+          }
+        }
+      };
+      static_for([&](auto ic) __attribute__((always_inline)) {
+        if constexpr (decltype(ic)::value < NM) fetch(ic);
+      }, std::make_integer_sequence<int, C::PREFETCH>{});
+      __builtin_amdgcn_sched_barrier(0);
+      static_for([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + C::PREFETCH < NM) fetch(std::integral_constant<int, i + C::PREFETCH>{});
+        mfma_i(ic);
+        __builtin_amdgcn_sched_barrier(0);
+      }, std::make_integer_sequence<int, NM>{});
+      // No instruction crosses the cluster boundaries (the scheduler would
+      // otherwise hoist the start of the VALU cluster above the barrier, into
+      // the MFMA cluster, where it waits on the statistics loads).
+      wait_vmem();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!LAST) valu(s);
+      if (qh == 1 && s + 2 < nsteps) copy_tile(s + 2, prev);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int p = 1, prev = 0;
+    for (int s = 1; s < nsteps; ++s) {
+      step(std::false_type{}, s, p, prev);
+      prev = p;
+      p = p == 2 ? 0 : p + 1;
+    }
+    step(std::true_type{}, nsteps, p, prev);
+    if (qh == 0) __syncthreads();
+
+    // ---- Sum the two groups' partial dK^T, dV^T through LDS (lane-contiguous
     // fp32, conflict-free) and store dK = scale * dK^T, dV = dV^T (one key
-    // per lane; 4 consecutive d per store). Every Q / dO read of this key
-    // tile finished before the last barrier.
+    // per lane; 4 consecutive d per store). Every read of the Q / dO buffers
+    // finished before the last barrier, and no copy is in flight.
     float* red = reinterpret_cast<float*>(qo_lds) + kb * (DB * 16 * 64) + lane;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
@@ -392,7 +506,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
       }
-      __syncthreads();   // the buffers are read (then refilled) again after this
+      __syncthreads();
     }
   }
 }
