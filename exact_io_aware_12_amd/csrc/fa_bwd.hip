@@ -303,23 +303,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vmem();
     __syncthreads();
 
-    // S = Q K^T and dP = dO V^T for this wave's 32 queries of the tile in
-    // buffer b x its 32 keys. aq / ak: row-major read offsets of this wave's
-    // query rows in buffer b / of its key rows, k-step 0.
-    auto sdp = [&](int aq, int ak) __attribute__((always_inline)) {
-      sacc = zero16();
-      pacc = zero16();
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int oq = aq ^ (ks << 5), ok = ak ^ (ks << 5);
-        const bf16x8 a_q = *reinterpret_cast<const bf16x8*>(qbuf(0) + oq);
-        const bf16x8 a_o = *reinterpret_cast<const bf16x8*>(obuf(0) + oq);
-        const bf16x8 b_k = *reinterpret_cast<const bf16x8*>(k_lds + ok);
-        const bf16x8 b_v = *reinterpret_cast<const bf16x8*>(v_lds + ok);
-        sacc = mfma_32x32x16(a_q, b_k, sacc);
-        pacc = mfma_32x32x16(a_o, b_v, pacc);
-      }
-    };
     // -LSE*log2(e) and D of this wave's rows of tile `step`, one row per
     // lane: lane l holds row 8*((l%16)/4) + 4*(l/32) + l%4, which is the row
     // of accumulator element l%16 in lane l's half of the wave, so element i
@@ -373,9 +356,65 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     };
 
-    // Prologue: every wave forms P, dS of tile 0.
+    // The MFMA cluster as an explicit software pipeline: MFMAs 0 .. NDV-1
+    // are dV^T / dK^T of the previous tile (A: transposing reads of dO / Q at
+    // atb, B: the packed P / dS), then 2*KS MFMAs are S and dP of the current
+    // tile in k-step pairs (A: Q / dO rows at aqb, B: K / V rows at ak). The
+    // operands of MFMA i + PREFETCH are read before MFMA i is issued, and
+    // scheduling barriers keep that order (left to itself, the scheduler may
+    // spend the look-ahead on reads needed much later).
+    auto mcluster = [&](auto with_dvdk, auto with_sdp, int atb, int aqb, int ak) __attribute__((always_inline)) {
+      constexpr int NDV = decltype(with_dvdk)::value ? 4 * DB : 0;
+      constexpr int NM = NDV + (decltype(with_sdp)::value ? 2 * KS : 0);
+      constexpr int PF = C::PREFETCH;
+      bf16x8 opa[PF + 1], opb[PF + 1];
+      auto fetch = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int r = i % (PF + 1);
+        if constexpr (i < NDV) {
+          constexpr int t = i / (2 * DB), db = (i / 2) % DB, isk = i % 2;
+          const int o0 = atb ^ (db << 6), o1 = (o0 ^ 32) + 8 * RB;
+          opa[r] = tr_operand((isk ? qbuf(0) : obuf(0)) + 16 * t * RB, o0, o1);
+        } else {
+          constexpr int j = i - NDV, ks = j / 2, isp = j % 2;
+          const int oq = aqb ^ (ks << 5), ok = ak ^ (ks << 5);
+          opa[r] = *reinterpret_cast<const bf16x8*>((isp ? obuf(0) : qbuf(0)) + oq);
+          opb[r] = *reinterpret_cast<const bf16x8*>((isp ? v_lds : k_lds) + ok);
+        }
+      };
+      auto mfma_i = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int r = i % (PF + 1);
+        if constexpr (i < NDV) {
+          constexpr int t = i / (2 * DB), db = (i / 2) % DB, isk = i % 2;
+          if constexpr (isk) dkacc[db] = mfma_32x32x16(opa[r], sbv[t], dkacc[db]);
+          else dvacc[db] = mfma_32x32x16(opa[r], pbv[t], dvacc[db]);
+        } else {
+          constexpr int j = i - NDV, isp = j % 2;
+          if constexpr (j < 2) {
+            if constexpr (isp) pacc = mfma_32x32x16(opa[r], opb[r], zero16());
+            else sacc = mfma_32x32x16(opa[r], opb[r], zero16());
+          } else {
+            if constexpr (isp) pacc = mfma_32x32x16(opa[r], opb[r], pacc);
+            else sacc = mfma_32x32x16(opa[r], opb[r], sacc);
+          }
+        }
+      };
+      static_for([&](auto ic) __attribute__((always_inline)) {
+        if constexpr (decltype(ic)::value < NM) fetch(ic);
+      }, std::make_integer_sequence<int, PF>{});
+      __builtin_amdgcn_sched_barrier(0);
+      static_for([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + PF < NM) fetch(std::integral_constant<int, i + PF>{});
+        mfma_i(ic);
+        __builtin_amdgcn_sched_barrier(0);
+      }, std::make_integer_sequence<int, NM>{});
+    };
+
+    // Prologue: every wave forms S, dP and then P, dS of tile 0.
     load_stats(0);
-    sdp(rq0 + 32 * qh * RB, rq0 + 32 * kb * RB);
+    mcluster(std::false_type{}, std::true_type{}, 0, rq0 + 32 * qh * RB, rq0 + 32 * kb * RB);
     valu(0);
     __syncthreads();
     // Group 1 starts one barrier later: its first slot copies tile 2.
@@ -398,58 +437,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       int aq = rq0 + 32 * qh * RB, ak = rq0 + 32 * kb * RB, at = tq0 + 32 * qh * RB;
       asm volatile("" : "+v"(aq), "+v"(ak), "+v"(at));
       if constexpr (!LAST) load_stats(s);
-      // The MFMA cluster as an explicit software pipeline: MFMAs 0 .. 4*DB-1
-      // are dV^T / dK^T of tile s-1 (A: transposing reads of dO / Q, B: the
-      // packed P / dS), then, unless this is the last step, S and dP of tile
-      // s in k-step pairs (A: Q / dO rows, B: K / V rows). The operands of
-      // MFMA i + PREFETCH are read before MFMA i is issued, and scheduling
-      // barriers keep that order (left to itself, the scheduler may spend
-      // the look-ahead on reads needed much later).
-      constexpr int NM = 4 * DB + (LAST ? 0 : 2 * KS);
-      const int atb = at + prev * C::QTILE, aqb = aq + p * C::QTILE;
-      bf16x8 opa[C::PREFETCH + 1], opb[C::PREFETCH + 1];
-      auto fetch = [&](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        constexpr int r = i % (C::PREFETCH + 1);
-        if constexpr (i < 4 * DB) {
-          constexpr int t = i / (2 * DB), db = (i / 2) % DB, isk = i % 2;
-          const int o0 = atb ^ (db << 6), o1 = (o0 ^ 32) + 8 * RB;
-          opa[r] = tr_operand((isk ? qbuf(0) : obuf(0)) + 16 * t * RB, o0, o1);
-        } else {
-          constexpr int j = i - 4 * DB, ks = j / 2, isp = j % 2;
-          const int oq = aqb ^ (ks << 5), ok = ak ^ (ks << 5);
-          opa[r] = *reinterpret_cast<const bf16x8*>((isp ? obuf(0) : qbuf(0)) + oq);
-          opb[r] = *reinterpret_cast<const bf16x8*>((isp ? v_lds : k_lds) + ok);
-        }
-      };
-      auto mfma_i = [&](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        constexpr int r = i % (C::PREFETCH + 1);
-        if constexpr (i < 4 * DB) {
-          constexpr int t = i / (2 * DB), db = (i / 2) % DB, isk = i % 2;
-          if constexpr (isk) dkacc[db] = mfma_32x32x16(opa[r], sbv[t], dkacc[db]);
-          else dvacc[db] = mfma_32x32x16(opa[r], pbv[t], dvacc[db]);
-        } else {
-          constexpr int j = i - 4 * DB, isp = j % 2;
-          if constexpr (j < 2) {
-            if constexpr (isp) pacc = mfma_32x32x16(opa[r], opb[r], zero16());
-            else sacc = mfma_32x32x16(opa[r], opb[r], zero16());
-          } else {
-            if constexpr (isp) pacc = mfma_32x32x16(opa[r], opb[r], pacc);
-            else sacc = mfma_32x32x16(opa[r], opb[r], sacc);
-          }
-        }
-      };
-      static_for([&](auto ic) __attribute__((always_inline)) {
-        if constexpr (decltype(ic)::value < NM) fetch(ic);
-      }, std::make_integer_sequence<int, C::PREFETCH>{});
-      __builtin_amdgcn_sched_barrier(0);
-      static_for([&](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i + C::PREFETCH < NM) fetch(std::integral_constant<int, i + C::PREFETCH>{});
-        mfma_i(ic);
-        __builtin_amdgcn_sched_barrier(0);
-      }, std::make_integer_sequence<int, NM>{});
+      mcluster(std::true_type{}, std::integral_constant<bool, !LAST>{}, at + prev * C::QTILE,
+               aq + p * C::QTILE, ak);
       // No instruction crosses the cluster boundaries (the scheduler would
       // otherwise hoist the start of the VALU cluster above the barrier, into
       // the MFMA cluster, where it waits on the statistics loads).
