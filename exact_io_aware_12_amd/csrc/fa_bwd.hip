@@ -83,6 +83,8 @@ struct BwdCfg {
   static_assert(6 * QTILE + 2 * VTILE <= 160 * 1024, "LDS");
   // The partial dK (then dV) sums of group 1 go through the Q / dO buffers.
   static_assert(4 * 16 * DB * 64 * 4 <= 6 * QTILE, "partial sums fit the Q/dO buffers");
+  // The bf16 gradients are staged row-major in the K and V tiles.
+  static_assert(BNK * RB <= VTILE && (BNK * RB / 16) % THREADS == 0, "staging");
 };
 
 // Swizzled byte offset of 2-byte element (row, col) in a tile with R-byte
@@ -461,38 +463,60 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     step(std::true_type{}, nsteps, p, prev);
     if (qh == 0) __syncthreads();
 
-    // ---- Sum the two groups' partial dK^T, dV^T through LDS (lane-contiguous
-    // fp32, conflict-free) and store dK = scale * dK^T, dV = dV^T (one key
-    // per lane; 4 consecutive d per store). Every read of the Q / dO buffers
-    // finished before the last barrier, and no copy is in flight.
-    float* red = reinterpret_cast<float*>(qo_lds) + kb * (DB * 16 * 64) + lane;
+    // ---- Sum the two groups' partial dK^T, dV^T and store them. For each
+    // gradient: group 1 writes its partial into the Q / dO ring (fp32,
+    // lane-contiguous 16-byte chunks: conflict-free); group 0 adds it to its
+    // own, scales (dK = scale * dK^T), rounds to bf16 and writes the rows
+    // row-major into the K (dK) or V (dV) tile, 16-byte chunks XOR-swizzled
+    // by the row so that a wave's 32 rows spread over the banks; then all 8
+    // waves store whole rows, 16 bytes per lane (coalesced). Group 1 writes
+    // the dV partial while dK is being stored. Every LDS read of this key
+    // tile finished before the last barrier, and no copy is in flight.
+    {
+      constexpr int CPR = RB / 16;                 // 16-byte chunks per row
+      // The lane indices are re-derived here (an empty asm hides that they
+      // are the kernel's), so that no address of this phase is computed
+      // early and held across the query-tile loop.
+      int t_id = tid;
+      asm volatile("" : "+v"(t_id));
+      const int ln = t_id & 63;
+      f32x4* part_w = reinterpret_cast<f32x4*>(qo_lds) + kb * (DB * 4 * 64) + ln;
+      const int row = 32 * kb + (ln & 31);         // this lane's row of the key tile
+      const int hh = ln >> 5;
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      f32x16 (&acc)[DB] = which == 0 ? dkacc : dvacc;
-      if (qh == 1) {
+      for (int which = 0; which < 2; ++which) {
+        f32x16 (&acc)[DB] = which == 0 ? dkacc : dvacc;
+        uint8_t* stage = which == 0 ? k_lds : v_lds;
+        if (qh == 1) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) red[(db * 16 + i) * 64] = acc[db][i];
-      }
-      __syncthreads();
-      if (qh == 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] += red[(db * 16 + i) * 64];
-        if (kk < N) {
-          uint16_t* row = (which == 0 ? dK : dV) + off + (size_t)kk * D;
+            for (int g4 = 0; g4 < 4; ++g4)
+              part_w[(db * 4 + g4) * 64] = f32x4{acc[db][4 * g4], acc[db][4 * g4 + 1],
+                                                 acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]};
+        }
+        __syncthreads();
+        if (qh == 0) {
           const float sc = which == 0 ? scale : 1.f;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-              const int d0 = db * 32 + 8 * g4 + 4 * hi;
-              u32x2 pk = {pack_bf16x2(acc[db][4 * g4] * sc, acc[db][4 * g4 + 1] * sc),
-                          pack_bf16x2(acc[db][4 * g4 + 2] * sc, acc[db][4 * g4 + 3] * sc)};
-              *reinterpret_cast<u32x2*>(row + d0) = pk;
+              const f32x4 o = part_w[(db * 4 + g4) * 64];
+              const int c = (4 * db + g4) ^ (row & (CPR - 1));
+              *reinterpret_cast<u32x2*>(stage + row * RB + c * 16 + 8 * hh) =
+                  u32x2{pack_bf16x2((acc[db][4 * g4] + o[0]) * sc, (acc[db][4 * g4 + 1] + o[1]) * sc),
+                        pack_bf16x2((acc[db][4 * g4 + 2] + o[2]) * sc, (acc[db][4 * g4 + 3] + o[3]) * sc)};
             }
+        }
+        __syncthreads();
+        uint16_t* dst = (which == 0 ? dK : dV) + off;
+#pragma unroll
+        for (int j = 0; j < C::BNK * CPR / C::THREADS; ++j) {
+          const int idx = t_id + j * C::THREADS;
+          const int r = idx / CPR, c = idx % CPR;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * RB + ((c ^ (r & (CPR - 1))) * 16));
+          if (k0 + r < N) *reinterpret_cast<u32x4*>(dst + (size_t)(k0 + r) * D + c * 8) = v;
         }
       }
       __syncthreads();
