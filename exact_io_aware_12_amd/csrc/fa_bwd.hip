@@ -746,18 +746,18 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int i = 0; i < 16; ++i) dqacc[db][i] += red[(db * 16 + i) * 64];
   }
 
-  // ---- dQ = scale * dQ^T (one query per lane; 4 consecutive d per store).
-  if (qrow < N) {
-    uint16_t* qrow_p = dQ + off + (size_t)qrow * D;
+  // ---- dQ = scale * dQ^T, out through this wave's slice of group 0's V
+  // buffers (free: every step ended with a barrier after its reads and
+  // copies, and the group sum above used the K buffers).
+  {
+    u32x2 qv[DB][4];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hi;
-        u32x2 pr = {pack_bf16x2(dqacc[db][4 * g4 + 0] * scale, dqacc[db][4 * g4 + 1] * scale),
-                    pack_bf16x2(dqacc[db][4 * g4 + 2] * scale, dqacc[db][4 * g4 + 3] * scale)};
-        *reinterpret_cast<u32x2*>(qrow_p + d0) = pr;
-      }
+      for (int g4 = 0; g4 < 4; ++g4)
+        qv[db][g4] = u32x2{pack_bf16x2(dqacc[db][4 * g4 + 0] * scale, dqacc[db][4 * g4 + 1] * scale),
+                           pack_bf16x2(dqacc[db][4 * g4 + 2] * scale, dqacc[db][4 * g4 + 3] * scale)};
+    store_rows_staged<D>(dQ + off + (size_t)qw * D, N - qw, &v_lds[0][0][0] + w * 32 * RB, qv, lane);
   }
 }
 

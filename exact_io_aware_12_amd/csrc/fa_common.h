@@ -84,4 +84,35 @@ __device__ __forceinline__ u32x4 ld_global_16B(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// One wave's 32 output rows (rows 0 .. 31 from `rows`, a row-major [*, D]
+// bf16 array), held one row per lane in accumulator layout: lane l has row l % 32
+// and d = 32*db + 8*g4 + 4*(l/32) .. +3 in v[db][g4]. Storing them directly
+// would scatter each 8-byte store over 32 rows. Instead they go through this
+// wave's own LDS slice `stage` (32 rows of 2*D bytes, 16-byte chunks
+// XOR-swizzled by the row so that one write's 32 rows spread over the banks)
+// and leave as whole rows, 16 bytes per lane, consecutive lanes on
+// consecutive chunks of a row. Rows from nvalid on are not stored. A wave's
+// LDS operations run in order, so no barrier is needed; no other wave may
+// use `stage` meanwhile.
+template <int D>
+__device__ __forceinline__ void store_rows_staged(uint16_t* rows, int nvalid, uint8_t* stage,
+                                                  const u32x2 (&v)[D / 32][4], int lane) {
+  constexpr int RB = 2 * D, CPR = RB / 16;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c = (4 * db + g4) ^ (r & (CPR - 1));
+      *reinterpret_cast<u32x2*>(stage + r * RB + c * 16 + 8 * h) = v[db][g4];
+    }
+#pragma unroll
+  for (int j = 0; j < 32 * CPR / 64; ++j) {
+    const int idx = lane + 64 * j;
+    const int rr = idx / CPR, cc = idx % CPR;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(stage + rr * RB + ((cc ^ (rr & (CPR - 1))) * 16));
+    if (rr < nvalid) *reinterpret_cast<u32x4*>(rows + (size_t)rr * D + cc * 8) = val;
+  }
+}
+
 }  // namespace fa

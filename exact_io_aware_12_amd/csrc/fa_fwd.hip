@@ -496,22 +496,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
-  // ---- epilogue: O = O / l, LSE = ln2 * (m + log2 l).
+  // ---- epilogue: O = O / l, LSE = ln2 * (m + log2 l). O leaves through
+  // this wave's slice of the K buffers (free: every step ended with a
+  // barrier after its reads and copies).
   const float l_tot = halves_sum(l_run);
-  if (qrow < N) {
+  {
     const float inv = 1.f / l_tot;
-    uint16_t* orow = O + off + (size_t)qrow * D;
+    u32x2 ov[C::DB][4];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hi;
-        u32x2 pr = {pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
-                    pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = pr;
-      }
-    if (hi == 0) LSE[(size_t)head * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+      for (int g4 = 0; g4 < 4; ++g4)
+        ov[db][g4] = u32x2{pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                           pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+    store_rows_staged<D>(O + off + (size_t)qw * D, N - qw, (w < 2 ? k_lds0 : k_lds1) + (w & 1) * 32 * C::RB,
+                         ov, lane);
   }
+  if (qrow < N && hi == 0) LSE[(size_t)head * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool POS>
@@ -794,22 +795,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   if (grp == 0) __syncthreads();
   wait_dma();
+  // Every wave's copies have landed and every read is done: the four tile
+  // buffers hold the 8 waves' O rows on their way out (8 KiB per wave).
+  __syncthreads();
 
   const float l_tot = halves_sum(l_run);
-  if (qrow < N) {
+  {
     const float inv = 1.f / l_tot;
-    uint16_t* orow = O + off + (size_t)qrow * D;
+    u32x2 ov[C::DB][4];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hi;
-        u32x2 pr = {pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
-                    pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = pr;
-      }
-    if (hi == 0) LSE[(size_t)head * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+      for (int g4 = 0; g4 < 4; ++g4)
+        ov[db][g4] = u32x2{pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                           pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+    uint8_t* const buf = blk < 2 ? kl0 : blk < 4 ? kl1 : blk < 6 ? vl0 : vl1;
+    store_rows_staged<D>(O + off + (size_t)qw * D, N - qw, buf + (blk & 1) * 32 * RB, ov, lane);
   }
+  if (qrow < N && hi == 0) LSE[(size_t)head * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
 template <bool CAUSAL, bool POS>
