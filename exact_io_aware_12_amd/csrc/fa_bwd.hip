@@ -587,31 +587,36 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   dma_rows<D, C::LOADS>(K + off, k_lds[grp][0], min(grp, nt - 1) * C::BN, N, w, lane);
   dma_rows<D, C::LOADS>(V + off, v_lds[grp][0], min(grp, nt - 1) * C::BN, N, w, lane);
+  // The tile's Q rows (and, with two groups, its dO rows) go to LDS by
+  // coalesced copies, 64 rows per buffer, into the second buffers (free until
+  // the first step's copies): loaded one row per lane, every 16-byte load
+  // would be spread over 32 rows. Rows past N read row N-1.
+  if constexpr (G == 2) {
+    dma_rows<D, C::LOADS>(Q + off, k_lds[grp][1], q0 + 64 * grp, N, w, lane);
+    dma_rows<D, C::LOADS>(dO + off, v_lds[grp][1], q0 + 64 * grp, N, w, lane);
+  } else {
+    dma_rows<D, C::LOADS>(Q + off, k_lds[0][1], q0, N, w, lane);
+    dma_rows<D, C::LOADS>(Q + off, v_lds[0][1], q0 + 64, N, w, lane);
+  }
 
-  // This lane's Q and dO rows as B operands (k-slots = head dim), and its
-  // row statistics: LSE in log2 units and D = dO . O (B1), summed over the
-  // lane's half of the row and exchanged with the other half. D is also
-  // written out for the dK / dV kernel, which runs after this one.
+  // This lane's Q and dO rows as B operands (k-slots = head dim), read from
+  // the staged tiles after the first barrier (with one group, dO straight
+  // from memory), and its row statistics: LSE in log2 units and D = dO . O
+  // (B1), summed over the lane's half of the row and exchanged with the
+  // other half. D is also written out for the dK / dV kernel, which runs
+  // after this one. The O row chunks load meanwhile.
   bf16x8 qreg[KS], doreg[KS];
-  float dpart = 0.f;
+  u32x4 oreg[KS];
   {
     const size_t o = off + (size_t)qc * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(Q + o + ks * 16));
-      doreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(dO + o + ks * 16));
-      const u32x4 ov = ld_global_16B(O + o + ks * 16);
-      const u32x4 dv = __builtin_bit_cast(u32x4, doreg[ks]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dpart += __uint_as_float(ov[e] << 16) * __uint_as_float(dv[e] << 16);
-        dpart += __uint_as_float(ov[e] & 0xffff0000u) * __uint_as_float(dv[e] & 0xffff0000u);
-      }
+      oreg[ks] = ld_global_16B(O + o + ks * 16);
+      if constexpr (G == 1) doreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(dO + o + ks * 16));
     }
   }
   const float nlse2 = -LSE[(size_t)head * N + qc] * kLog2e;
-  const float drow = halves_sum(dpart);
-  if (grp == 0 && hi == 0 && qrow < N) Dvec[(size_t)head * N + qrow] = drow;
+  float drow = 0.f;
 
   // Per-lane LDS offsets (the swizzle only looks at bits 0-3 of the row, so
   // 16- and 32-row steps are immediates): row-major reads of row l32 (K and
@@ -695,6 +700,32 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   wait_vmem();
+  __syncthreads();
+  {
+    // Rows 32w .. 32w+31 of the tile: in the first buffer for w < 2.
+    const int h = w >> 1;
+    const uint8_t* qs = G == 2 ? k_lds[h][1] : (h == 0 ? k_lds[0][1] : v_lds[0][1]);
+    const uint8_t* ds = v_lds[h][1];
+    const int row = 32 * (w & 1) + l32;
+    float dpart = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int o = sw_off<RB>(row, 16 * ks + 8 * hi);
+      qreg[ks] = *reinterpret_cast<const bf16x8*>(qs + o);
+      if constexpr (G == 2) doreg[ks] = *reinterpret_cast<const bf16x8*>(ds + o);
+      const u32x4 ov = oreg[ks];
+      const u32x4 dv = __builtin_bit_cast(u32x4, doreg[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dpart += __uint_as_float(ov[e] << 16) * __uint_as_float(dv[e] << 16);
+        dpart += __uint_as_float(ov[e] & 0xffff0000u) * __uint_as_float(dv[e] & 0xffff0000u);
+      }
+    }
+    drow = halves_sum(dpart);
+    if (grp == 0 && hi == 0 && qrow < N) Dvec[(size_t)head * N + qrow] = drow;
+  }
+  // Every wave has its rows before the first step's copies refill the
+  // second buffers.
   __syncthreads();
 
   // Step s: group g computes key tile j = G*s + g and copies its next tile
