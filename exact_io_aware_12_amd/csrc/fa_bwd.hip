@@ -288,6 +288,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     };
 
+    // -LSE*log2(e) and D of this wave's rows of tile `step`, one row per
+    // lane: lane l holds row 8*((l%16)/4) + 4*(l/32) + l%4, which is the row
+    // of accumulator element l%16 in lane l's half of the wave, so element i
+    // takes its value from lane i of its 16-lane row (a DPP broadcast). Rows
+    // past N read row N-1 (their P is zero). Issued at the start of the MFMA
+    // cluster, used in the VALU cluster (tile 0's: with the prologue copies).
+    float nlse_l, d_l;
+    const int srow = 8 * ((lane & 15) >> 2) + 4 * hi + (lane & 3);
+    auto load_stats = [&](int step) __attribute__((always_inline)) {
+      const int r = min(tile_at(step) * C::BMQ + 32 * qh + srow, N - 1);
+      nlse_l = LSEh[r];
+      d_l = Dh[r];
+    };
     // Prologue: this key tile's K and V, query tiles 0 and 1 (all waves).
     dma_rows<D, C::VLOADS>(K + off, k_lds, k0, N, w, lane);
     dma_rows<D, C::VLOADS>(V + off, v_lds, k0, N, w, lane);
@@ -297,6 +310,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       dma_rows<D, C::QLOADS>(Qh, qbuf(1), tile_at(1) * C::BMQ, N, w, lane);
       dma_rows<D, C::QLOADS>(dOh, obuf(1), tile_at(1) * C::BMQ, N, w, lane);
     }
+    load_stats(0);
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
       dkacc[i] = zero16();
@@ -305,19 +319,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vmem();
     __syncthreads();
 
-    // -LSE*log2(e) and D of this wave's rows of tile `step`, one row per
-    // lane: lane l holds row 8*((l%16)/4) + 4*(l/32) + l%4, which is the row
-    // of accumulator element l%16 in lane l's half of the wave, so element i
-    // takes its value from lane i of its 16-lane row (a DPP broadcast). Rows
-    // past N read row N-1 (their P is zero). Issued at the start of the MFMA
-    // cluster, used in the VALU cluster.
-    float nlse_l, d_l;
-    const int srow = 8 * ((lane & 15) >> 2) + 4 * hi + (lane & 3);
-    auto load_stats = [&](int step) __attribute__((always_inline)) {
-      const int r = min(tile_at(step) * C::BMQ + 32 * qh + srow, N - 1);
-      nlse_l = LSEh[r];
-      d_l = Dh[r];
-    };
     // P and dS of tile `step` from sacc / pacc, packed (registers 8t .. 8t+7:
     // the k-slot order of the dV / dK B operands).
     auto valu = [&](int step) __attribute__((always_inline)) {
@@ -415,7 +416,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // Prologue: every wave forms S, dP and then P, dS of tile 0.
-    load_stats(0);
     mcluster(std::false_type{}, std::true_type{}, 0, rq0 + 32 * qh * RB, rq0 + 32 * kb * RB);
     valu(0);
     __syncthreads();
