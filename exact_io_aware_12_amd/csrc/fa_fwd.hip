@@ -546,6 +546,16 @@ static hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_
 // of 64 keys are double-buffered in LDS (64 KiB, so every operand read keeps
 // an immediate offset); group 1 issues every tile copy, in its VALU
 // clusters, and waits for it at the end of its next MFMA cluster.
+//
+// SPLIT (grids of at most one 128-row tile per CU): both groups own the same
+// 128 query rows and split the key tiles between them, group g taking tiles
+// g, g+2, g+4, ... into its own half of each buffer (128 KiB) and copying
+// them itself. Each group's softmax statistics and O are partial; at the end
+// group 1 passes its max, row sums and O accumulators through LDS and group 0
+// rescales both parts to the larger max (exp2 of the differences), adds them
+// and stores. On such grids the one-group kernel leaves one wave per SIMD
+// with nothing to overlap with; here two waves of each SIMD alternate MFMA
+// and VALU clusters, and the longest row's key tiles are shared by two waves.
 // ---------------------------------------------------------------------------
 struct PingPongCfg {
   static constexpr int D = 128, BM = 256, THREADS = 512, BN = 64, RB = 256;
@@ -555,7 +565,7 @@ struct PingPongCfg {
 };
 
 
-template <bool CAUSAL, bool POS>
+template <bool CAUSAL, bool POS, bool SPLIT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_pp_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
@@ -563,17 +573,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   using C = PingPongCfg;
   using FC = FwdCfg<128>;
   constexpr int D = C::D, RB = C::RB, BN = C::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t kl0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kl1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vl0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vl1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kl0[(SPLIT ? 2 : 1) * C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kl1[(SPLIT ? 2 : 1) * C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vl0[(SPLIT ? 2 : 1) * C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vl1[(SPLIT ? 2 : 1) * C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wall = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wall >> 2;            // 0: waves 0-3, 1: waves 4-7 (wave i and i+4 share a SIMD)
   const int w = wall & 3;               // wave within the group
-  const int blk = 2 * w + grp;          // this wave's 32-row block of the 256 rows
+  // SPLIT: both groups own the same 128 rows (block w) and take alternate key
+  // tiles (group g: local tile j is key tile 2j + g), each in its own half of
+  // every LDS buffer; the two partial results are merged at the end.
+  const int blk = SPLIT ? w : 2 * w + grp;   // this wave's 32-row block
+  constexpr int BMQ = SPLIT ? 128 : C::BM;   // query rows per workgroup
+  const int gofs = SPLIT ? grp * C::TILE : 0;
   const int l32 = lane & 31, hi = lane >> 5;
 
   int head, rank;
@@ -589,16 +604,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   const int qt = CAUSAL ? (ntq - 1 - rank) : rank;
-  const int q0 = qt * C::BM;
+  const int q0 = qt * BMQ;
   const int qw = q0 + 32 * blk;
   const int qrow = qw + l32;
   const size_t off = (size_t)head * N * D;
   const uint16_t* Kh = K + off;
   const uint16_t* Vh = V + off;
 
-  const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
+  const int kend = CAUSAL ? min(N, q0 + BMQ) : N;
   const int nt = (kend + BN - 1) / BN;
-  const int ntw = CAUSAL ? min(nt, (min(N, qw + 32) + BN - 1) / BN) : nt;
+  const int ntw_all = CAUSAL ? min(nt, (min(N, qw + 32) + BN - 1) / BN) : nt;
+  // Steps (the same for every wave) and this wave's computed local tiles.
+  const int ns = SPLIT ? (nt + 1) >> 1 : nt;
+  const int ntw = SPLIT ? (ntw_all - grp + 1) >> 1 : ntw_all;
+  auto key_tile = [&](int j) { return SPLIT ? 2 * j + grp : j; };
 
   static_assert(FC::LOADS == C::LOADS, "copy layout shared with fa_fwd_kernel");
   // This group's 4 waves copy tile t (tiles past the last repeat it: in
@@ -607,14 +626,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // are formed here, in the VALU cluster, rather than held in registers.
   auto copy_tile = [&](auto is_v, uint8_t* dst, int t) __attribute__((always_inline)) {
     constexpr bool IS_V = decltype(is_v)::value;
-    const int kb0 = min(t, nt - 1) * BN;
+    const int kb0 = min(key_tile(t), nt - 1) * BN;
     const int rmax = N - 1 - kb0;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int r = dma_row<128, IS_V>(w, i, lane);
       const uint32_t o = (uint32_t)(min(r, rmax) * D + dma_col<128, IS_V>(r, lane)) * 2u;
       lds_copy16((IS_V ? Vh : Kh) + (size_t)kb0 * D, o,
-                 lds_addr_of(dst + (w * C::LOADS + i) * 1024));
+                 lds_addr_of(dst + gofs + (w * C::LOADS + i) * 1024));
     }
   };
   using KT = std::integral_constant<bool, false>;
@@ -627,8 +646,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ks = 0; ks < C::KS; ++ks)
       qreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(qp + ks * 16));
   }
-  // Prologue copies: K_0 and K_1 (group 0), V_0 and V_1 (group 1).
-  if (grp == 0) {
+  // Prologue copies: K_0 and K_1 (group 0), V_0 and V_1 (group 1); with
+  // SPLIT every group copies its own four.
+  if (SPLIT) {
+    copy_tile(KT{}, kl0, 0);
+    copy_tile(KT{}, kl1, 1);
+    copy_tile(VT{}, vl0, 0);
+    copy_tile(VT{}, vl1, 1);
+  } else if (grp == 0) {
     copy_tile(KT{}, kl0, 0);
     copy_tile(KT{}, kl1, 1);
   } else {
@@ -638,13 +663,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int koff[C::KS];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = k_off<D>(l32, 2 * ks + hi);
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = k_off<D>(l32, 2 * ks + hi) + gofs;
   int voff[C::DB];
   {
     const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
-      voff[db] = v_off<D>(4 * hi + (sl >> 2), 32 * db + 16 * (g & 1) + 4 * (sl & 3));
+      voff[db] = v_off<D>(4 * hi + (sl >> 2), 32 * db + 16 * (g & 1) + 4 * (sl & 3)) + gofs;
   }
 
   f32x16 oacc[C::DB];
@@ -758,15 +783,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   wait_dma();
   __syncthreads();
   // Prologue: every wave forms P_0 from K_0.
-  scores(kl0);
-  softmax(0);
+  if (!SPLIT || ntw > 0) {
+    scores(kl0);
+    softmax(key_tile(0) * BN);
+  }
   __syncthreads();
   // Group 1 starts one cluster later: its first slot copies K_2 into K_0's
-  // buffer (free now) and waits for it; group 0 meanwhile runs M(0).
+  // buffer (free now) and waits for it; group 0 meanwhile runs M(0). With
+  // SPLIT group 0 copies its own K_2 there too, waited for at the end of M(0).
   if (grp == 1) {
     copy_tile(KT{}, kl0, 2);
     wait_dma();
     __syncthreads();
+  } else if (SPLIT) {
+    copy_tile(KT{}, kl0, 2);
   }
 
   // Every wave runs the same clusters: M(j), barrier, V(j), barrier. With
@@ -782,22 +812,56 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint8_t* const v_fill = P ? vl1 : vl0;         // V_j's buffer, gets V_{j+2}
     mcluster(j, k_next, v_this);
     __syncthreads();
-    if (j + 1 < ntw) softmax((j + 1) * BN);
-    if (grp == 1) {
+    if (j + 1 < ntw) softmax(key_tile(j + 1) * BN);
+    if (SPLIT || grp == 1) {
       copy_tile(KT{}, k_fill, j + 3);
       copy_tile(VT{}, v_fill, j + 2);
     }
     __syncthreads();
   };
-  for (int j = 0; j < nt; j += 2) {
+  for (int j = 0; j < ns; j += 2) {
     step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
+    if (j + 1 < ns) step(std::integral_constant<int, 1>{}, j + 1);
   }
   if (grp == 0) __syncthreads();
   wait_dma();
   // Every wave's copies have landed and every read is done: the four tile
   // buffers hold the 8 waves' O rows on their way out (8 KiB per wave).
   __syncthreads();
+
+  if constexpr (SPLIT) {
+    // Group 1 hands its reference max, its row-half sums and its O^T partials
+    // to the group-0 wave with the same rows and lanes (through its own LDS
+    // halves), which rescales both to the larger max and adds them.
+    float* const xo = reinterpret_cast<float*>((w == 0 ? kl0 : w == 1 ? kl1 : w == 2 ? vl0 : vl1) + C::TILE);
+    float* const xs = reinterpret_cast<float*>(vl1) + w * 128;
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(xo + ((db * 4 + q4) * 64 + lane) * 4) =
+              f32x4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
+      xs[lane] = m_run;
+      xs[64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xs[lane], l1 = xs[64 + lane];
+    const float m = vmax(m_run, m1);
+    const float mu = m == -INFINITY ? 0.f : m;
+    const float a0 = fast_exp2(m_run - mu), a1 = fast_exp2(m1 - mu);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 p = *reinterpret_cast<const f32x4*>(xo + ((db * 4 + q4) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[db][4 * q4 + e] = fmaf(p[e], a1, oacc[db][4 * q4 + e] * a0);
+      }
+    l_run = fmaf(l1, a1, l_run * a0);
+    m_run = m;
+  }
 
   const float l_tot = halves_sum(l_run);
   {
@@ -815,15 +879,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (qrow < N && hi == 0) LSE[(size_t)head * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
-template <bool CAUSAL, bool POS>
+template <bool CAUSAL, bool POS, bool SPLIT = false>
 static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 uint16_t* o, float* lse, int BH, int N, float scale,
                                 hipStream_t stream) {
-  const int ntq = (N + PingPongCfg::BM - 1) / PingPongCfg::BM;
+  const int bmq = SPLIT ? 128 : PingPongCfg::BM;
+  const int ntq = (N + bmq - 1) / bmq;
   const int xcd_group = (BH % 8 == 0) ? BH / 8 : 0;
   const float c2 = scale * kLog2e;
   dim3 grid((unsigned)(ntq * BH)), block(PingPongCfg::THREADS);
-  hipLaunchKernelGGL((fa_fwd_pp_kernel<CAUSAL, POS>), grid, block, 0, stream,
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<CAUSAL, POS, SPLIT>), grid, block, 0, stream,
                      q, k, v, o, lse, BH, N, ntq, c2, xcd_group);
   return hipGetLastError();
 }
@@ -834,6 +899,15 @@ static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint
 // not; B=2, H=32, N=4096 non-causal), but 5-14 % slower on shorter causal
 // sequences (N = 4096, 2048), where its 256-row workgroups leave SIMDs idle
 // across a 4-tile diagonal that a second, independent workgroup would fill.
+// d = 128 grids of at most 256 128-row query tiles (one per CU) with at least
+// 1024 keys take the two-group kernel with the keys split between the groups:
+// measured 11-15 % faster causal (B=1 with H=8, N=4096; H=4, N=8192; H=2,
+// N=16384) and 2-5 % non-causal (H=8, N=4096; H=2, N=16384). With 512 tiles
+// (B=2, H=16, N=2048) the split kernel needs two rounds and is 11 % slower.
+bool fwd_uses_split_kernel(int BH, int N, int d) {
+  return d == 128 && N >= 1024 && (long)((N + 127) / 128) * BH <= 256;
+}
+
 bool fwd_uses_two_group_kernel(int BH, int N, int d, bool causal) {
   return d == 128 && (long)((N + PingPongCfg::BM - 1) / PingPongCfg::BM) * BH >= 256 &&
          N >= (causal ? 8192 : 4096);
@@ -843,6 +917,12 @@ hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* o, float* lse, int BH, int N, int d, float scale,
                         bool causal, hipStream_t stream) {
   const bool pos = scale > 0.f;
+  if (fwd_uses_split_kernel(BH, N, d)) {
+    if (causal && pos) return launch_fwd_pp<true, true, true>(q, k, v, o, lse, BH, N, scale, stream);
+    if (!causal && pos) return launch_fwd_pp<false, true, true>(q, k, v, o, lse, BH, N, scale, stream);
+    if (causal && !pos) return launch_fwd_pp<true, false, true>(q, k, v, o, lse, BH, N, scale, stream);
+    return launch_fwd_pp<false, false, true>(q, k, v, o, lse, BH, N, scale, stream);
+  }
   if (fwd_uses_two_group_kernel(BH, N, d, causal)) {
     if (causal && pos) return launch_fwd_pp<true, true>(q, k, v, o, lse, BH, N, scale, stream);
     if (!causal && pos) return launch_fwd_pp<false, true>(q, k, v, o, lse, BH, N, scale, stream);

@@ -307,6 +307,24 @@ def test_fwd_two_group_kernel(fa, N, H, causal, scale, heads):
     _check_fwd_sampled(fa, 1, H, N, 128, causal, seed=6000 + N, heads=heads, scale=scale)
 
 
+# d = 128 grids of at most 256 128-row query tiles take the two-group kernel
+# with the key tiles split between the groups and the two partial results
+# merged at the end. Ragged lengths (last 64-key tile partial), both mask
+# modes, a negative and a zero scale, and the largest such grid; every row of
+# every (or the sampled) head.
+@pytest.mark.parametrize("N,H,causal,scale,heads", [
+    (1500, 3, True, None, None),
+    (1025, 2, False, None, None),
+    (2000, 2, True, -0.21, None),
+    (1024, 4, False, 0.0, [3]),
+    (16384, 2, True, None, [1]),
+])
+def test_fwd_split_key_kernel(fa, N, H, causal, scale, heads):
+    assert fa.fa_fwd_kernel_name(1, H, N, 128, causal).startswith("fa_fwd_pp_kernel (keys split")
+    _check_fwd_sampled(fa, 1, H, N, 128, causal, seed=7000 + N, heads=heads if heads is not None else list(range(H)),
+                       scale=scale)
+
+
 # ---------------------------------------------------------------- long context
 @pytest.mark.parametrize("N,H,d", [(65536, 2, 128), (100003, 1, 64)])
 def test_fwd_long_context_sampled_rows(fa, N, H, d):
