@@ -41,6 +41,9 @@ def parse():
                    help="approximate CPU time budget of the oracle sample")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--fwd-shape", default=None, metavar="B,H,N,d,causal",
+                   help="instead of the fused step, time the forward alone on seeded N(0,1) "
+                        "bf16 inputs of this shape (scale 1/sqrt(d)) and print one JSON line")
     p.add_argument("--decode", choices=["d1", "d8"], default=None,
                    help="instead of the fused step, time decode attention (Nq query rows "
                         "against a KV cache) on this decode workload; HBM-bound")
@@ -159,6 +162,48 @@ def cpu_baseline(w, inp, budget_s):
     }
 
 
+def run_fwd_shape(args):
+    """Forward alone on one shape: HIP events around each call, on the launch stream."""
+    import numpy as np
+    import torch
+    from exact_io_aware_12_amd import fa
+    from exact_io_aware_12_amd import inputs as fi
+    B, H, N, d, causal = (int(x) for x in args.fwd_shape.split(","))
+    causal = bool(causal)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.library()
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(fi.random_bf16((B, H, N, d), 9100 + i).view(np.int16)).view(torch.bfloat16).to(dev)
+               for i in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record(stream)
+        fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    avg = sum(ms) / len(ms)
+    flops = 4.0 * B * H * N * N * d / (2 if causal else 1)
+    tf = flops / (avg * 1e-3) / 1e12
+    print(json.dumps({"metric": "attention fwd TFLOP/s (bf16)", "value": round(tf, 2), "unit": "TFLOP/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(avg, 4),
+                      "median_ms": round(median(ms), 4), "min_ms": round(min(ms), 4),
+                      "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": f"fwd_b{B}h{H}n{N}d{d}{'_causal' if causal else ''}",
+                                 "B": B, "H": H, "N": N, "d": d, "causal": causal},
+                      "kernel": fa.fa_fwd_kernel_name(B, H, N, d, causal),
+                      "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+
+
 def run_decode(args):
     """Decode attention: value = K/V bytes read per call / call time (GB/s)."""
     import numpy as np
@@ -253,6 +298,9 @@ def main():
 
     if args.decode is not None:
         run_decode(args)
+        return
+    if args.fwd_shape is not None:
+        run_fwd_shape(args)
         return
 
     import numpy as np
