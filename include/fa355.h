@@ -76,12 +76,16 @@ FA355_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float
            int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
- * Name of the kernel fa_fwd launches for this shape: "fa_fwd_kernel" (128-row
- * query tiles, two independent 4-wave workgroups per CU) or
- * "fa_fwd_pp_kernel" (long d = 128 sequences: 256-row workgroups whose two
- * 4-wave groups alternate MFMA and VALU clusters). Both compute the same
- * values. NULL when the shape is invalid. The string is static; no GPU is
- * touched.
+ * Name of the kernel fa_fwd launches for this shape:
+ *   "fa_fwd_kernel": 128-row query tiles, two independent 4-wave workgroups
+ *     per CU;
+ *   "fa_fwd_pp_kernel": long d = 128 sequences, 256-row workgroups whose two
+ *     4-wave groups alternate MFMA and VALU clusters;
+ *   "fa_fwd_pp_kernel (keys split between the groups)": d = 128, N >= 1024
+ *     and at most 256 query tiles of 128 rows; both groups own the same 128
+ *     rows, take alternate key tiles and merge their partial results.
+ * All compute the same values up to the order of fp32 sums. NULL when the
+ * shape is invalid. The string is static; no GPU is touched.
  */
 FA355_API const char* fa_fwd_kernel_name(int B, int H, int N, int d, int causal);
 
