@@ -51,7 +51,9 @@ def test_fwd_kernel_name_follows_the_dispatch_rule(fa):
     assert fa.fa_fwd_kernel_name(1, 3, 1500, 128, True) == split
     assert fa.fa_fwd_kernel_name(1, 3, 16384, 128, True) == "fa_fwd_kernel"   # 384 tiles, 192 of 256 rows
     assert fa.fa_fwd_kernel_name(1, 2, 1000, 128, True) == "fa_fwd_kernel"    # N < 1024
-    assert fa.fa_fwd_kernel_name(1, 1, 16384, 64, True) == "fa_fwd_kernel"    # d = 64
+    assert fa.fa_fwd_kernel_name(1, 3, 16384, 64, True) == "fa_fwd_kernel"    # d = 64, 384 tiles
+    assert fa.fa_fwd_kernel_name(1, 1, 16384, 64, True) == "fa_fwd_kernel (keys split between two groups)"
+    assert fa.fa_fwd_kernel_name(4, 16, 2048, 64, True) == "fa_fwd_kernel"    # 1024 tiles
     assert fa.fa_fwd_kernel_name(1, 16, 16384, 64, True) == "fa_fwd_kernel"      # d = 64
     assert fa.fa_fwd_kernel_name(0, 16, 16384, 128, True) is None
     assert fa.fa_fwd_kernel_name(1, 16, 16384, 96, True) is None

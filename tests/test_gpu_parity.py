@@ -325,6 +325,22 @@ def test_fwd_split_key_kernel(fa, N, H, causal, scale, heads):
                        scale=scale)
 
 
+# The same split at d = 64 (4-wave groups of fa_fwd_kernel in one 8-wave
+# workgroup): ragged N, both mask modes, negative and zero scales, the
+# largest such grid.
+@pytest.mark.parametrize("N,H,causal,scale,heads", [
+    (1500, 3, True, None, None),
+    (1025, 2, False, None, None),
+    (2000, 2, True, -0.21, None),
+    (1024, 4, False, 0.0, [3]),
+    (16384, 2, True, None, [1]),
+])
+def test_fwd_split_groups_d64(fa, N, H, causal, scale, heads):
+    assert fa.fa_fwd_kernel_name(1, H, N, 64, causal) == "fa_fwd_kernel (keys split between two groups)"
+    _check_fwd_sampled(fa, 1, H, N, 64, causal, seed=7100 + N, heads=heads if heads is not None else list(range(H)),
+                       scale=scale)
+
+
 # ---------------------------------------------------------------- long context
 @pytest.mark.parametrize("N,H,d", [(65536, 2, 128), (100003, 1, 64)])
 def test_fwd_long_context_sampled_rows(fa, N, H, d):
