@@ -806,10 +806,13 @@ static hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     // A causal grid that fits in one round (two 4-wave workgroups per CU on
     // 256 CUs) takes as long as its longest query tile's chain of key tiles:
     // then each tile's key tiles are split over two groups of 4 waves in one
-    // workgroup (measured at B=2, H=16, N=2048: -5 us of about 150).
+    // workgroup (measured at B=2, H=16, N=2048: -5 us of about 150). So is a
+    // non-causal grid of at most one 4-wave workgroup per CU, which would
+    // leave one wave per SIMD (backward -5.5 % at B=1, H=8, N=4096 and
+    // H=2, N=16384); with two per CU the split is 3 % slower there.
     bool split = false;
-    if constexpr (CAUSAL) {
-      if (ntq * BH <= 512) {
+    {
+      if (ntq * BH <= (CAUSAL ? 512 : 256)) {
         split = true;
         hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, 2>), grid, dim3(2 * C::THREADS), 0,
                            stream, q, k, v, dout, o, lse, dvec, dq, BH, N, ntq, scale * kLog2e,
