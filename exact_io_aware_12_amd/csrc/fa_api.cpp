@@ -15,6 +15,7 @@ hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 bool fwd_uses_two_group_kernel(int BH, int N, int d, bool causal);
 bool fwd_uses_split_kernel(int BH, int N, int d);
 bool fwd_uses_split_groups(int BH, int N, int d);
+bool bwd_dq_uses_split(int BH, int N, bool causal);
 hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* o, const uint16_t* dout, const float* lse,
                         uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec, int BH, int N,
@@ -73,6 +74,13 @@ const char* fa_fwd_kernel_name(int B, int H, int N, int d, int causal) {
   if (fa::fwd_uses_split_groups(B * H, N, d)) return "fa_fwd_kernel (keys split between two groups)";
   return fa::fwd_uses_two_group_kernel(B * H, N, d, causal != 0) ? "fa_fwd_pp_kernel"
                                                                  : "fa_fwd_kernel";
+}
+
+const char* fa_bwd_kernel_name(int B, int H, int N, int d, int causal) {
+  if (check_shape(B, H, N, d) != FA_OK) return nullptr;
+  return fa::bwd_dq_uses_split(B * H, N, causal != 0)
+             ? "fa_bwd_dq_kernel (keys split between two groups) + fa_bwd_dkdv_kernel"
+             : "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel";
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {

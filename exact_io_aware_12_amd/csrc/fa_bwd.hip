@@ -792,6 +792,16 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// The dQ kernel's key split (two 4-wave groups per 128-query tile taking
+// alternate key tiles): causal grids of at most 512 query tiles (one round at
+// two workgroups per CU), non-causal grids of at most 256 (one per CU). The
+// same rule for both head dimensions.
+bool bwd_dq_uses_split(int BH, int N, bool causal) {
+  const int ntq = (N + DqCfg<128>::BM - 1) / DqCfg<128>::BM;
+  static_assert(DqCfg<128>::BM == DqCfg<64>::BM, "one query-tile size");
+  return (int64_t)ntq * BH <= (causal ? 512 : 256);
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const uint16_t* o, const uint16_t* dout, const float* lse,
@@ -810,16 +820,11 @@ static hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     // non-causal grid of at most one 4-wave workgroup per CU, which would
     // leave one wave per SIMD (backward -5.5 % at B=1, H=8, N=4096 and
     // H=2, N=16384); with two per CU the split is 3 % slower there.
-    bool split = false;
-    {
-      if (ntq * BH <= (CAUSAL ? 512 : 256)) {
-        split = true;
-        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, 2>), grid, dim3(2 * C::THREADS), 0,
-                           stream, q, k, v, dout, o, lse, dvec, dq, BH, N, ntq, scale * kLog2e,
-                           scale, xcd_group);
-      }
-    }
-    if (!split)
+    if (bwd_dq_uses_split(BH, N, CAUSAL))
+      hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, 2>), grid, dim3(2 * C::THREADS), 0,
+                         stream, q, k, v, dout, o, lse, dvec, dq, BH, N, ntq, scale * kLog2e,
+                         scale, xcd_group);
+    else
       hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, 1>), grid, dim3(C::THREADS), 0, stream,
                          q, k, v, dout, o, lse, dvec, dq, BH, N, ntq, scale * kLog2e, scale,
                          xcd_group);

@@ -6,7 +6,7 @@ the C ABI, and every step of the computation runs in the library's kernels.
 PyTorch only supplies device memory and the stream. There is no fallback: if
 the library cannot be loaded, every call raises.
 
-The functions ``fa_fwd``, ``fa_fwd_kernel_name``, ``fa_bwd``, ``fa_bwd_workspace_bytes``,
+The functions ``fa_fwd``, ``fa_fwd_kernel_name``, ``fa_bwd``, ``fa_bwd_kernel_name``, ``fa_bwd_workspace_bytes``,
 ``fa_unfused_fwd``, ``fa_unfused_workspace_bytes``, ``fa_fa1_fwd``,
 ``fa_fa1_workspace_bytes``, ``fa_decode_fwd``,
 ``fa_decode_workspace_bytes`` and ``fa_strerror`` are the raw C entry points
@@ -55,6 +55,8 @@ def _load():
     lib.fa_fwd.restype = i
     lib.fa_fwd_kernel_name.argtypes = [i, i, i, i, i]
     lib.fa_fwd_kernel_name.restype = ctypes.c_char_p
+    lib.fa_bwd_kernel_name.argtypes = [i, i, i, i, i]
+    lib.fa_bwd_kernel_name.restype = ctypes.c_char_p
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
@@ -96,6 +98,12 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, 
 def fa_fwd_kernel_name(B, H, N, d, causal) -> str | None:
     """Name of the kernel fa_fwd launches for this shape (None if invalid)."""
     r = _load().fa_fwd_kernel_name(B, H, N, d, int(bool(causal)))
+    return r.decode() if r is not None else None
+
+
+def fa_bwd_kernel_name(B, H, N, d, causal) -> str | None:
+    """Names of the kernels fa_bwd launches for this shape (None if invalid)."""
+    r = _load().fa_bwd_kernel_name(B, H, N, d, int(bool(causal)))
     return r.decode() if r is not None else None
 
 

@@ -122,6 +122,18 @@ FA355_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            float scale, int causal, void* stream);
 
 /*
+ * Names of the two kernels fa_bwd launches for this shape, in launch order:
+ *   "fa_bwd_dq_kernel (keys split between two groups) + fa_bwd_dkdv_kernel"
+ *     when the dQ grid is small (causal: at most 512 query tiles of 128 rows;
+ *     non-causal: at most 256): two 4-wave groups per query tile take
+ *     alternate key tiles and add their partial dQ in a fixed order;
+ *   "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel" otherwise.
+ * Both compute the same values up to the order of fp32 sums. NULL when the
+ * shape is invalid. The string is static; no GPU is touched.
+ */
+FA355_API const char* fa_bwd_kernel_name(int B, int H, int N, int d, int causal);
+
+/*
  * Unfused ("standard") attention: the same O and LSE as fa_fwd, computed by
  * the three-step decomposition that the fused pass avoids, kept as a
  * measured comparator. Method: the interview answer's "standard attention"

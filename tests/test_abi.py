@@ -32,7 +32,8 @@ def fa():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_fwd",
+    assert _declared() == ["fa_bwd", "fa_bwd_kernel_name", "fa_bwd_workspace_bytes",
+                           "fa_decode_fwd",
                            "fa_decode_workspace_bytes", "fa_fa1_fwd", "fa_fa1_workspace_bytes",
                            "fa_fwd", "fa_fwd_kernel_name", "fa_strerror", "fa_unfused_fwd",
                            "fa_unfused_workspace_bytes"]
@@ -57,6 +58,22 @@ def test_fwd_kernel_name_follows_the_dispatch_rule(fa):
     assert fa.fa_fwd_kernel_name(1, 16, 16384, 64, True) == "fa_fwd_kernel"      # d = 64
     assert fa.fa_fwd_kernel_name(0, 16, 16384, 128, True) is None
     assert fa.fa_fwd_kernel_name(1, 16, 16384, 96, True) is None
+
+
+def test_bwd_kernel_name_follows_the_dispatch_rule(fa):
+    # dQ key split: causal grids of at most 512 query tiles of 128 rows,
+    # non-causal grids of at most 256; both head dimensions.
+    split = "fa_bwd_dq_kernel (keys split between two groups) + fa_bwd_dkdv_kernel"
+    plain = "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel"
+    for d in (64, 128):
+        assert fa.fa_bwd_kernel_name(2, 16, 2048, d, True) == split     # 512 tiles
+        assert fa.fa_bwd_kernel_name(2, 16, 2048, d, False) == plain    # 512 > 256
+        assert fa.fa_bwd_kernel_name(1, 33, 1000, d, False) == plain    # 264 > 256
+        assert fa.fa_bwd_kernel_name(1, 32, 1024, d, False) == split    # 256
+        assert fa.fa_bwd_kernel_name(4, 33, 500, d, True) == plain      # 528 > 512
+        assert fa.fa_bwd_kernel_name(1, 1, 1, d, False) == split
+    assert fa.fa_bwd_kernel_name(1, 1, 16, 96, True) is None
+    assert fa.fa_bwd_kernel_name(1, 0, 16, 64, True) is None
 
 
 def test_every_declared_symbol_is_exported():
@@ -142,7 +159,6 @@ def test_bwd_workspace(fa):
 @pytest.mark.parametrize("which", ["q", "dout", "lse", "dv"])
 def test_bwd_align(fa, which):
     assert _bwd(fa, **{which: GOOD + 4}) == fa.FA_ERR_ALIGN
-    assert _bwd(fa, ws=GOOD + 8) == fa.FA_ERR_ALIGN
 
 
 def test_bwd_shape_and_scale(fa):

@@ -10,8 +10,8 @@ import pytest
 
 import oracle
 from exact_io_aware_12_amd import inputs as fi
-from parity_util import (TOL_GRAD, TOL_LSE, TOL_O, assert_close, bits_to_f64, from_gpu,
-                         to_gpu_bf16)
+from parity_util import (TOL_GRAD, TOL_LSE, TOL_O, assert_close, assert_close_rel, bits_to_f64,
+                         from_gpu, map_heads, to_gpu_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -145,9 +145,12 @@ def test_fwd_deterministic_and_stream(fa):
 
 
 # ---------------------------------------------------------------- backward
-def _check_bwd(fa, B, H, N, d, causal, seed, scale=None):
+def _check_bwd(fa, B, H, N, d, causal, seed, scale=None, relative=False):
+    """Backward against the oracle: the absolute bound at 1/sqrt(d) (and at
+    scales that shrink the gradients), the relative form otherwise."""
     import torch
-    print(f"[bwd] B={B} H={H} N={N} d={d} causal={causal} seed={seed}", flush=True)
+    print(f"[bwd] B={B} H={H} N={N} d={d} causal={causal} seed={seed} scale={scale} "
+          f"kernels={fa.fa_bwd_kernel_name(B, H, N, d, causal)}", flush=True)
     shape = (B, H, N, d)
     qb, kb, vb, dob = (fi.random_bf16(shape, seed + i) for i in range(4))
     scale = 1 / math.sqrt(d) if scale is None else scale
@@ -155,11 +158,17 @@ def _check_bwd(fa, B, H, N, d, causal, seed, scale=None):
     do = to_gpu_bf16(dob)
     dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    rq, rk, rv = oracle.attention_bwd(bits_to_f64(qb), bits_to_f64(kb), bits_to_f64(vb),
-                                      bits_to_f64(dob), scale, causal)
-    assert_close("dQ", from_gpu(dq), rq, TOL_GRAD)
-    assert_close("dK", from_gpu(dk), rk, TOL_GRAD)
-    assert_close("dV", from_gpu(dv), rv, TOL_GRAD)
+    fq, fk, fv, fdo = (bits_to_f64(x) for x in (qb, kb, vb, dob))
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    ref = map_heads(lambda bh: oracle.attention_bwd(fq[bh], fk[bh], fv[bh], fdo[bh], scale,
+                                                    causal), heads)
+    got = [from_gpu(t) for t in (dq, dk, dv)]
+    for i, name in enumerate(("dQ", "dK", "dV")):
+        r = np.stack([x[i] for x in ref]).reshape(shape)
+        if relative:
+            assert_close_rel(name, got[i], r)
+        else:
+            assert_close(name, got[i], r, TOL_GRAD)
 
 
 # Causal grids of at most 512 query tiles split each tile's key tiles between
@@ -197,11 +206,49 @@ def test_fwd_bwd_tile_edges(fa, N, d, causal):
     _check_bwd(fa, 1, 2, N, d, causal, seed=5000 + N + d)
 
 
+DQ_PLAIN = "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel"
+DQ_SPLIT = "fa_bwd_dq_kernel (keys split between two groups) + fa_bwd_dkdv_kernel"
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_causal_unsplit_grid(fa, d):
     # 4 query tiles x 132 heads = 528 > 512: the causal dQ kernel without the
     # key split; N = 500 leaves a ragged last tile.
+    assert fa.fa_bwd_kernel_name(4, 33, 500, d, True) == DQ_PLAIN
     _check_bwd(fa, 4, 33, 500, d, True, seed=2500 + d)
+
+
+# Non-causal grids above 256 query tiles take the dQ kernel without the key
+# split: 8 tiles x 33 heads = 264 with a ragged last tile (N = 1000), and the
+# fwd+bwd workload's shape run non-causally (512 tiles). Every head.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", [(1, 33, 1000), (2, 16, 2048)])
+def test_bwd_noncausal_unsplit_grid(fa, B, H, N, d):
+    assert fa.fa_bwd_kernel_name(B, H, N, d, False) == DQ_PLAIN
+    _check_bwd(fa, B, H, N, d, False, seed=2600 + N + d)
+
+
+# The largest non-causal grid that still takes the key split (256 tiles).
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_noncausal_split_largest_grid(fa, d):
+    assert fa.fa_bwd_kernel_name(1, 32, 1024, d, False) == DQ_SPLIT
+    _check_bwd(fa, 1, 32, 1024, d, False, seed=2700 + d)
+
+
+# Positive scales other than 1/sqrt(d) (0.37 and 0.25: gradients several times
+# larger than at 1/sqrt(d)), checked by the relative form of the bound, on
+# both dQ variants, both mask modes and ragged lengths.
+@pytest.mark.parametrize("B,H,N,causal,d,scale", [
+    (1, 2, 385, True, 128, 0.37),     # split dQ
+    (1, 2, 385, False, 128, 0.37),
+    (1, 2, 193, True, 64, 0.37),
+    (1, 2, 255, False, 64, 0.25),
+    (4, 33, 500, True, 128, 0.37),    # unsplit dQ, causal
+    (1, 33, 1000, False, 128, 0.25),  # unsplit dQ, non-causal
+    (1, 33, 1000, False, 64, 0.37),
+])
+def test_bwd_other_positive_scales(fa, B, H, N, causal, d, scale):
+    _check_bwd(fa, B, H, N, d, causal, seed=2800 + N + d, scale=scale, relative=True)
 
 
 def test_bwd_deterministic(fa):
@@ -222,7 +269,8 @@ def test_bwd_scale_zero_and_negative(fa):
 
 
 # ---------------------------------------------------------------- the five workloads
-def _workload_fwd(fa, idx, heads=None):
+def _workload_fwd(fa, idx):
+    """Every element of every head against the oracle."""
     import torch
     inp = fi.make_inputs(idx)
     w = inp.workload
@@ -232,11 +280,13 @@ def _workload_fwd(fa, idx, heads=None):
     torch.cuda.synchronize()
     o_np, l_np = from_gpu(o), from_gpu(lse)
     sel = [(b, h) for b in range(w.B) for h in range(w.H)]
-    if heads is not None:
-        sel = [sel[i] for i in heads]
-    for b, h in sel:
-        ro, rl = oracle.attention_fwd(bits_to_f64(inp.q[b, h]), bits_to_f64(inp.k[b, h]),
-                                      bits_to_f64(inp.v[b, h]), w.scale, w.causal)
+
+    def ref(bh):
+        b, h = bh
+        return oracle.attention_fwd(bits_to_f64(inp.q[b, h]), bits_to_f64(inp.k[b, h]),
+                                    bits_to_f64(inp.v[b, h]), w.scale, w.causal)
+
+    for (b, h), (ro, rl) in zip(sel, map_heads(ref, sel)):
         assert_close(f"O[{b},{h}]", o_np[b, h], ro, TOL_O)
         assert_close(f"LSE[{b},{h}]", l_np[b, h], rl, TOL_LSE)
     return inp, (q, k, v, o, lse)
@@ -250,31 +300,35 @@ def test_workload2_fwd(fa):
     _workload_fwd(fa, 2)
 
 
-def test_workload3_fwd_sampled_heads(fa):
-    # 64 heads; the oracle checks every row of 6 heads spread over both batches.
-    _workload_fwd(fa, 3, heads=[0, 13, 31, 32, 50, 63])
+def test_workload3_fwd(fa):
+    # 64 heads of 4096 rows, causal, d = 128.
+    _workload_fwd(fa, 3)
 
 
-def test_workload4_fwd_sampled_heads(fa):
-    # 16 heads of 16384 rows with K x 3; every row of the first and last head.
-    _workload_fwd(fa, 4, heads=[0, 15])
+def test_workload4_fwd(fa):
+    # 16 heads of 16384 rows with K x 3, causal, d = 128.
+    _workload_fwd(fa, 4)
 
 
 def test_workload5_fwd_bwd(fa):
     import torch
-    inp, (q, k, v, o, lse) = _workload_fwd(fa, 5, heads=[0, 17, 31])
+    inp, (q, k, v, o, lse) = _workload_fwd(fa, 5)
     w = inp.workload
     do = to_gpu_bf16(inp.do)
     dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=True, scale=w.scale)
     torch.cuda.synchronize()
     g = [from_gpu(t) for t in (dq, dk, dv)]
-    for b in range(w.B):
-        for h in range(w.H):
-            r = oracle.attention_bwd(bits_to_f64(inp.q[b, h]), bits_to_f64(inp.k[b, h]),
-                                     bits_to_f64(inp.v[b, h]), bits_to_f64(inp.do[b, h]),
-                                     w.scale, True)
-            for name, got, ref in zip(("dQ", "dK", "dV"), g, r):
-                assert_close(f"{name}[{b},{h}]", got[b, h], ref, TOL_GRAD)
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def ref(bh):
+        b, h = bh
+        return oracle.attention_bwd(bits_to_f64(inp.q[b, h]), bits_to_f64(inp.k[b, h]),
+                                    bits_to_f64(inp.v[b, h]), bits_to_f64(inp.do[b, h]),
+                                    w.scale, True)
+
+    for (b, h), r in zip(sel, map_heads(ref, sel)):
+        for name, got, rr in zip(("dQ", "dK", "dV"), g, r):
+            assert_close(f"{name}[{b},{h}]", got[b, h], rr, TOL_GRAD)
 
 
 # ---------------------------------------------------------------- two-group forward
@@ -302,8 +356,11 @@ def _check_fwd_sampled(fa, B, H, N, d, causal, seed, heads, scale=None):
     (8200, 32, True, None, [0, 31]),
     (4096, 64, False, -0.21, [5]),
     (8192, 32, True, 0.0, [9]),
+    (4096, 64, False, 0.3, [11]),
+    (8200, 32, True, 0.45, [30]),
 ])
 def test_fwd_two_group_kernel(fa, N, H, causal, scale, heads):
+    assert fa.fa_fwd_kernel_name(1, H, N, 128, causal) == "fa_fwd_pp_kernel"
     _check_fwd_sampled(fa, 1, H, N, 128, causal, seed=6000 + N, heads=heads, scale=scale)
 
 
@@ -318,6 +375,8 @@ def test_fwd_two_group_kernel(fa, N, H, causal, scale, heads):
     (2000, 2, True, -0.21, None),
     (1024, 4, False, 0.0, [3]),
     (16384, 2, True, None, [1]),
+    (1500, 3, True, 0.3, None),
+    (1025, 2, False, 0.45, None),
 ])
 def test_fwd_split_key_kernel(fa, N, H, causal, scale, heads):
     assert fa.fa_fwd_kernel_name(1, H, N, 128, causal).startswith("fa_fwd_pp_kernel (keys split")
@@ -334,6 +393,8 @@ def test_fwd_split_key_kernel(fa, N, H, causal, scale, heads):
     (2000, 2, True, -0.21, None),
     (1024, 4, False, 0.0, [3]),
     (16384, 2, True, None, [1]),
+    (1500, 3, True, 0.3, None),
+    (1025, 2, False, 0.45, None),
 ])
 def test_fwd_split_groups_d64(fa, N, H, causal, scale, heads):
     assert fa.fa_fwd_kernel_name(1, H, N, 64, causal) == "fa_fwd_kernel (keys split between two groups)"
