@@ -20,6 +20,8 @@ hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* o, const uint16_t* dout, const float* lse,
                         uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dvec, int BH, int N,
                         int d, float scale, bool causal, hipStream_t stream);
+size_t bwd_noalloc_max_rows();
+hipError_t bwd_noalloc_scratch(float** out);
 hipError_t unfused_fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 uint16_t* o, float* lse, float* ws, int BH, int N, int d,
                                 float scale, bool causal, hipStream_t stream, bool* blas_failed);
@@ -103,6 +105,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
   float* dvec = static_cast<float*>(workspace);
+  hipError_t e = fa::bwd_dispatch(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
+      static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dvec, B * H, N, d, scale,
+      causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                   int H, int N, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != FA_OK) return rc;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if ((size_t)B * H * N > fa::bwd_noalloc_max_rows()) return FA_ERR_TOO_LARGE;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  float* dvec = nullptr;
+  if (fa::bwd_noalloc_scratch(&dvec) != hipSuccess) return FA_ERR_HIP;
   hipError_t e = fa::bwd_dispatch(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
@@ -211,6 +235,8 @@ const char* fa_strerror(int code) {
     case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case FA_ERR_HIP: return "the HIP runtime reported a launch error";
     case FA_ERR_BLAS: return "rocBLAS reported an error (unfused comparator only)";
+    case FA_ERR_TOO_LARGE:
+      return "B*H*N exceeds the 4194304 rows of fa_bwd_noalloc's static scratch";
     default: return "unknown fa355 error code";
   }
 }

@@ -52,6 +52,7 @@
 //     work and the LDS operand reads of each phase. dK/dV kernel: its MFMA
 //     cluster is an explicit software pipeline (operands read a fixed number
 //     of MFMAs ahead, the order pinned by scheduling barriers).
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -839,6 +840,44 @@ static hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_
                        xcd_group);
   }
   return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- no-allocation scratch
+// Device memory for the row statistic D of fa_bwd_noalloc, for callers that
+// cannot allocate: a file-scope array that every device holds from the
+// library's load until the process ends (16 MiB). In host code the name
+// `scratch` is only a host-side handle; its device address is looked up once
+// per device with hipGetSymbolAddress and only that address is ever passed to
+// a kernel. Nothing in it needs clearing: the dQ kernel writes D for every
+// row of the call before the dK/dV kernel, on the same stream, reads it.
+constexpr size_t kNoAllocRows = size_t(1) << 22;
+static __device__ __align__(256) float scratch[kNoAllocRows];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+size_t bwd_noalloc_max_rows() { return kNoAllocRows; }
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with it current) and kept for the life of the process.
+hipError_t bwd_noalloc_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -6,7 +6,8 @@ the C ABI, and every step of the computation runs in the library's kernels.
 PyTorch only supplies device memory and the stream. There is no fallback: if
 the library cannot be loaded, every call raises.
 
-The functions ``fa_fwd``, ``fa_fwd_kernel_name``, ``fa_bwd``, ``fa_bwd_kernel_name``, ``fa_bwd_workspace_bytes``,
+The functions ``fa_fwd``, ``fa_fwd_kernel_name``, ``fa_bwd``, ``fa_bwd_noalloc``,
+``fa_bwd_kernel_name``, ``fa_bwd_workspace_bytes``,
 ``fa_unfused_fwd``, ``fa_unfused_workspace_bytes``, ``fa_fa1_fwd``,
 ``fa_fa1_workspace_bytes``, ``fa_decode_fwd``,
 ``fa_decode_workspace_bytes`` and ``fa_strerror`` are the raw C entry points
@@ -22,7 +23,8 @@ import os
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_SCALE, FA_ERR_ALIGN, \
-    FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_BLAS = range(9)
+    FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_BLAS, FA_ERR_TOO_LARGE = range(10)
+FA_BWD_NOALLOC_MAX_ROWS = 4194304
 
 
 class FAError(RuntimeError):
@@ -55,6 +57,8 @@ def _load():
     lib.fa_fwd.restype = i
     lib.fa_fwd_kernel_name.argtypes = [i, i, i, i, i]
     lib.fa_fwd_kernel_name.restype = ctypes.c_char_p
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_kernel_name.argtypes = [i, i, i, i, i]
     lib.fa_bwd_kernel_name.restype = ctypes.c_char_p
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
@@ -99,6 +103,12 @@ def fa_fwd_kernel_name(B, H, N, d, causal) -> str | None:
     """Name of the kernel fa_fwd launches for this shape (None if invalid)."""
     r = _load().fa_fwd_kernel_name(B, H, N, d, int(bool(causal)))
     return r.decode() if r is not None else None
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal,
+                   stream) -> int:
+    return _load().fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale,
+                                  int(causal), stream)
 
 
 def fa_bwd_kernel_name(B, H, N, d, causal) -> str | None:
@@ -226,6 +236,28 @@ def bwd(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None
                 B, H, N, d, float(scale), causal, _stream_ptr(q.device, stream))
     if rc != FA_OK:
         raise FAError(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, do, lse, *, causal: bool = False, scale: float | None = None,
+                dq, dk, dv, stream=None):
+    """``bwd`` through fa_bwd_noalloc: the caller passes the outputs; the
+    library's static scratch replaces the workspace (nothing is allocated)."""
+    import torch
+    _check(q, "q", dtype=torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, q.shape, torch.bfloat16)
+    _check(lse, "lse", (B, H, N), torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rc = fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                        B, H, N, d, float(scale), causal, _stream_ptr(q.device, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -62,8 +62,12 @@ enum {
   FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                  */
   FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required           */
   FA_ERR_HIP = 7,       /* the HIP runtime reported a launch error           */
-  FA_ERR_BLAS = 8       /* rocBLAS reported an error (fa_unfused_fwd only)   */
+  FA_ERR_BLAS = 8,      /* rocBLAS reported an error (fa_unfused_fwd only)   */
+  FA_ERR_TOO_LARGE = 9  /* B*H*N above FA_BWD_NOALLOC_MAX_ROWS               */
 };
+
+/* Largest B*H*N that fa_bwd_noalloc accepts (its static scratch: 16 MiB). */
+#define FA_BWD_NOALLOC_MAX_ROWS 4194304
 
 /*
  * Forward pass: O = softmax(scale * Q K^T [causal mask]) V and the per-row
@@ -120,6 +124,26 @@ FA355_API int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
            float scale, int causal, void* stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments, kernels and results as fa_bwd
+ * (bit-identical outputs); the row statistic D lives in a static device
+ * array of the library instead of the caller's workspace.
+ *   - B*H*N must be at most FA_BWD_NOALLOC_MAX_ROWS, else FA_ERR_TOO_LARGE
+ *     (checked before any HIP call).
+ *   - Allocates nothing: no hipMalloc/hipFree and no allocating library call.
+ *     The array (16 MiB) exists on every device the library is loaded on
+ *     until the process ends; its address is looked up once per device on
+ *     the first call there (a HIP error then gives FA_ERR_HIP).
+ *   - Every call on one device uses that device's one array: calls that
+ *     overlap in time on one device (two streams, two host threads) race and
+ *     give undefined gradients. Serialize them (one stream, or events).
+ */
+FA355_API int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
  * Names of the two kernels fa_bwd launches for this shape, in launch order:

@@ -32,8 +32,8 @@ def fa():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_bwd", "fa_bwd_kernel_name", "fa_bwd_workspace_bytes",
-                           "fa_decode_fwd",
+    assert _declared() == ["fa_bwd", "fa_bwd_kernel_name", "fa_bwd_noalloc",
+                           "fa_bwd_workspace_bytes", "fa_decode_fwd",
                            "fa_decode_workspace_bytes", "fa_fa1_fwd", "fa_fa1_workspace_bytes",
                            "fa_fwd", "fa_fwd_kernel_name", "fa_strerror", "fa_unfused_fwd",
                            "fa_unfused_workspace_bytes"]
@@ -86,7 +86,8 @@ def test_every_declared_symbol_is_exported():
 def test_codes_match_binding(fa):
     codes = _codes()
     assert codes["FA_OK"] == fa.FA_OK == 0
-    for n in ("NULL", "SHAPE", "HEADDIM", "SCALE", "ALIGN", "WORKSPACE", "HIP", "BLAS"):
+    for n in ("NULL", "SHAPE", "HEADDIM", "SCALE", "ALIGN", "WORKSPACE", "HIP", "BLAS",
+              "TOO_LARGE"):
         assert codes["FA_ERR_" + n] == getattr(fa, "FA_ERR_" + n)
         assert fa.fa_strerror(codes["FA_ERR_" + n]) not in ("", "unknown fa355 error code")
     assert fa.fa_strerror(99) == "unknown fa355 error code"
@@ -159,6 +160,41 @@ def test_bwd_workspace(fa):
 @pytest.mark.parametrize("which", ["q", "dout", "lse", "dv"])
 def test_bwd_align(fa, which):
     assert _bwd(fa, **{which: GOOD + 4}) == fa.FA_ERR_ALIGN
+
+
+# ------------------------------------------------ fa_bwd_noalloc (static scratch)
+def _bwd_na(fa, B=1, H=1, N=16, d=64, scale=0.125, **ptrs):
+    p = dict(q=GOOD, k=GOOD, v=GOOD, o=GOOD, dout=GOOD, lse=GOOD, dq=GOOD, dk=GOOD, dv=GOOD)
+    p.update(ptrs)
+    return fa.fa_bwd_noalloc(p["q"], p["k"], p["v"], p["o"], p["dout"], p["lse"], p["dq"],
+                             p["dk"], p["dv"], B, H, N, d, scale, 1, None)
+
+
+def test_noalloc_limit_matches_header(fa):
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+FA_BWD_NOALLOC_MAX_ROWS\s+(\d+)", text)
+    assert m and int(m.group(1)) == fa.FA_BWD_NOALLOC_MAX_ROWS == 1 << 22
+
+
+@pytest.mark.parametrize("B,H,N", [(1, 1, (1 << 22) + 1), (2, 32, 65537), (64, 64, 1025)])
+def test_noalloc_rejects_rows_beyond_the_scratch(fa, B, H, N):
+    # Rejected before any HIP call (no GPU here): too many rows for the
+    # 16 MiB static scratch, though the shape itself is valid for fa_bwd.
+    assert B * H * N > fa.FA_BWD_NOALLOC_MAX_ROWS
+    assert _bwd_na(fa, B=B, H=H, N=N) == fa.FA_ERR_TOO_LARGE
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"])
+def test_noalloc_null(fa, which):
+    assert _bwd_na(fa, **{which: None}) == fa.FA_ERR_NULL
+
+
+def test_noalloc_validation(fa):
+    assert _bwd_na(fa, d=96) == fa.FA_ERR_HEADDIM
+    assert _bwd_na(fa, N=0) == fa.FA_ERR_SHAPE
+    assert _bwd_na(fa, scale=math.nan) == fa.FA_ERR_SCALE
+    assert _bwd_na(fa, dk=GOOD + 2) == fa.FA_ERR_ALIGN
+    assert _bwd(fa, ws=GOOD + 8) == fa.FA_ERR_ALIGN
 
 
 def test_bwd_shape_and_scale(fa):
