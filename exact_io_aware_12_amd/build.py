@@ -1,5 +1,6 @@
-"""Build libfa355.so (the HIP kernels and the C ABI) for gfx950, in-tree, and
-the fa355_ceilings calibration program.
+"""Build libfa355.so (the HIP kernels and the C ABI) for gfx950, in-tree, the
+unfused comparator's libfa355_unfused.so (the only one linked with rocBLAS),
+and the fa355_ceilings calibration program.
 
 Usage: ``python -m exact_io_aware_12_amd.build`` (or ``__graft_entry__.build()``).
 Always recompiles. Needs only hipcc; no GPU is touched.
@@ -16,10 +17,13 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa355.so")
+# The unfused comparator: its own library, the only one linked with rocBLAS.
+LIB_UNFUSED = os.path.join(PKG, "libfa355_unfused.so")
 # Calibration program (unit ceilings measured on the device), not linked into
 # the library.
 CEILINGS = os.path.join(PKG, "fa355_ceilings")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_unfused.hip", "fa_fa1.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fa1.hip", "fa_api.cpp"]
+SOURCES_UNFUSED = ["fa_unfused.hip", "fa_unfused_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -39,20 +43,25 @@ def _compile(src: str, obj: str, extra: list[str]) -> None:
         sys.stderr.write("\n".join(noise) + "\n")
 
 
+def _link(objs: list[str], out: str, libs: list[str]) -> None:
+    cmd = [HIPCC, *COMMON, "-shared", *objs, "-o", out + ".tmp", *libs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(out + ".tmp", out)
+
+
 def build(extra: list[str] | None = None) -> str:
     extra = list(extra or [])
     tmp = tempfile.mkdtemp(prefix="fa355_build_")
     try:
-        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
-        with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-            list(ex.map(lambda a: _compile(a[0], a[1], extra), zip(SOURCES, objs)))
-        out_tmp = LIB + ".tmp"
-        # rocBLAS serves the two plain GEMMs of the unfused comparator.
-        cmd = [HIPCC, *COMMON, "-shared", *objs, "-o", out_tmp, "-L/opt/rocm/lib", "-lrocblas"]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-        os.replace(out_tmp, LIB)
+        srcs = SOURCES + SOURCES_UNFUSED
+        objs = {s: os.path.join(tmp, s + ".o") for s in srcs}
+        with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+            list(ex.map(lambda s: _compile(s, objs[s], extra), srcs))
+        _link([objs[s] for s in SOURCES], LIB, [])
+        # rocBLAS serves the two plain GEMMs of the unfused comparator only.
+        _link([objs[s] for s in SOURCES_UNFUSED], LIB_UNFUSED, ["-L/opt/rocm/lib", "-lrocblas"])
         cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, os.path.join(CSRC, "ceilings.hip"), "-o",
                CEILINGS + ".tmp"]
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/fa355.h"
+#include "fa_validate.h"
 
 namespace fa {
 hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -22,9 +23,6 @@ hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int d, float scale, bool causal, hipStream_t stream);
 size_t bwd_noalloc_max_rows();
 hipError_t bwd_noalloc_scratch(float** out);
-hipError_t unfused_fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                uint16_t* o, float* lse, float* ws, int BH, int N, int d,
-                                float scale, bool causal, hipStream_t stream, bool* blas_failed);
 size_t fa1_workspace_floats(int BH, int N, int d);
 hipError_t fa1_fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             uint16_t* o, float* lse, float* ws, int BH, int N, int d,
@@ -35,23 +33,10 @@ hipError_t decode_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t*
                            bool causal, hipStream_t stream);
 }  // namespace fa
 
-namespace {
-
-constexpr int64_t kMaxElems = 2147483647;  // 2^31 - 1
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-int check_shape(int B, int H, int N, int d) {
-  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  const int64_t elems = (int64_t)B * H * N * d;
-  if (elems > kMaxElems) return FA_ERR_SHAPE;
-  return FA_OK;
-}
-
-size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-}  // namespace
+using fa::aligned16;
+using fa::check_shape;
+using fa::kMaxElems;
+using fa::round256;
 
 extern "C" {
 
@@ -133,33 +118,6 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
       static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dvec, B * H, N, d, scale,
       causal != 0, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
-size_t fa_unfused_workspace_bytes(int B, int H, int N, int d) {
-  if (check_shape(B, H, N, d) != FA_OK) return 0;
-  return round256((size_t)B * H * N * (size_t)N * sizeof(float));
-}
-
-int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
-                   float scale, int causal, void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  int rc = check_shape(B, H, N, d);
-  if (rc != FA_OK) return rc;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
-  const size_t need = fa_unfused_workspace_bytes(B, H, N, d);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  const void* ptrs[] = {q, k, v, o, lse, workspace};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return FA_ERR_ALIGN;
-  bool blas_failed = false;
-  hipError_t e = fa::unfused_fwd_dispatch(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
-      static_cast<float*>(workspace), B * H, N, d, scale, causal != 0,
-      static_cast<hipStream_t>(stream), &blas_failed);
-  if (blas_failed) return FA_ERR_BLAS;
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

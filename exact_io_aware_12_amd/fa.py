@@ -1,4 +1,5 @@
-"""Thin ctypes binding of libfa355.so (fused exact attention for gfx950).
+"""Thin ctypes binding of libfa355.so (fused exact attention for gfx950) and of
+the unfused comparator's libfa355_unfused.so.
 
 Argument marshalling only: tensors are checked for device, dtype, shape and
 contiguity, their device pointers and torch's current HIP stream are passed to
@@ -21,6 +22,10 @@ import math
 import os
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
+# The unfused comparator (rocBLAS GEMMs) is a library of its own, opened only
+# when one of its entry points is called.
+_LIB_UNFUSED_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                 "libfa355_unfused.so")
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_SCALE, FA_ERR_ALIGN, \
     FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_BLAS, FA_ERR_TOO_LARGE = range(10)
@@ -65,10 +70,6 @@ def _load():
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
-    lib.fa_unfused_workspace_bytes.argtypes = [i, i, i, i]
-    lib.fa_unfused_workspace_bytes.restype = sz
-    lib.fa_unfused_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
-    lib.fa_unfused_fwd.restype = i
     lib.fa_fa1_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_fa1_workspace_bytes.restype = sz
     lib.fa_fa1_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
@@ -83,9 +84,35 @@ def _load():
     return lib
 
 
+_lib_unfused = None
+
+
+def _load_unfused():
+    global _lib_unfused
+    if _lib_unfused is not None:
+        return _lib_unfused
+    _load()   # the fused library (and torch's HIP runtime) first
+    if not os.path.exists(_LIB_UNFUSED_PATH):
+        raise ImportError(f"{_LIB_UNFUSED_PATH} is missing: build it with "
+                          "`python -m exact_io_aware_12_amd.build`")
+    lib = ctypes.CDLL(_LIB_UNFUSED_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_unfused_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_unfused_workspace_bytes.restype = sz
+    lib.fa_unfused_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    lib.fa_unfused_fwd.restype = i
+    _lib_unfused = lib
+    return lib
+
+
 def library():
     """The loaded ctypes library (raises if it is missing)."""
     return _load()
+
+
+def library_unfused():
+    """The unfused comparator's ctypes library (raises if it is missing)."""
+    return _load_unfused()
 
 
 # ----------------------------------------------------------------- raw C ABI
@@ -123,12 +150,12 @@ def fa_bwd_workspace_bytes(B, H, N, d) -> int:
 
 def fa_unfused_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale, causal,
                    stream) -> int:
-    return _load().fa_unfused_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d,
-                                  scale, int(causal), stream)
+    return _load_unfused().fa_unfused_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H,
+                                          N, d, scale, int(causal), stream)
 
 
 def fa_unfused_workspace_bytes(B, H, N, d) -> int:
-    return _load().fa_unfused_workspace_bytes(B, H, N, d)
+    return _load_unfused().fa_unfused_workspace_bytes(B, H, N, d)
 
 
 def fa_fa1_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale, causal,

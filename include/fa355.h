@@ -31,9 +31,8 @@
  *   - Ownership: the caller allocates and frees every buffer, including the
  *     workspaces. fa_fwd and fa_bwd keep no state between calls, allocate no
  *     memory and are safe to call from several host threads. The unfused
- *     comparator (fa_unfused_fwd) creates one rocBLAS handle per device on
- *     its first call there (rocBLAS allocates its own scratch memory then)
- *     and keeps it until the process ends.
+ *     comparator lives in its own library (fa355_unfused.h,
+ *     libfa355_unfused.so) so that this one does not depend on rocBLAS.
  *   - Errors: 0 (FA_OK) on success, else one of the FA_ERR_* codes below.
  *     Arguments are validated before any HIP call, so an invalid call launches
  *     nothing and touches no memory. No C++ exception crosses this ABI.
@@ -62,7 +61,7 @@ enum {
   FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                  */
   FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required           */
   FA_ERR_HIP = 7,       /* the HIP runtime reported a launch error           */
-  FA_ERR_BLAS = 8,      /* rocBLAS reported an error (fa_unfused_fwd only)   */
+  FA_ERR_BLAS = 8,      /* rocBLAS reported an error (libfa355_unfused only) */
   FA_ERR_TOO_LARGE = 9  /* B*H*N above FA_BWD_NOALLOC_MAX_ROWS               */
 };
 
@@ -156,28 +155,6 @@ FA355_API int fa_bwd_noalloc(const void* q, const void* k, const void* v, const 
  * shape is invalid. The string is static; no GPU is touched.
  */
 FA355_API const char* fa_bwd_kernel_name(int B, int H, int N, int d, int causal);
-
-/*
- * Unfused ("standard") attention: the same O and LSE as fa_fwd, computed by
- * the three-step decomposition that the fused pass avoids, kept as a
- * measured comparator. Method: the interview answer's "standard attention"
- * steps and "FlashAttention and Triton" (chapter 19), section 19.2:
- *   1. S = scale * Q K^T is written to memory (fp32, library GEMM);
- *   2. a row-wise softmax pass (section 19.11: one workgroup per row, row
- *      max, exp, row sum) reads S, applies the causal mask and writes P
- *      (bf16) and the LSE;
- *   3. O = P V (library GEMM, fp32 accumulate, bf16 out).
- *   q, k, v, o, lse  : as for fa_fwd
- *   workspace        : device memory of workspace_bytes bytes, at least
- *                      fa_unfused_workspace_bytes(B,H,N,d): holds S as fp32
- *                      [B,H,N,N], then P as bf16 over the first half of each
- *                      S row; contents on return are unspecified.
- * Returns FA_ERR_BLAS when rocBLAS fails.
- */
-FA355_API size_t fa_unfused_workspace_bytes(int B, int H, int N, int d);
-FA355_API int fa_unfused_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-           void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
-           float scale, int causal, void* stream);
 
 /*
  * Decode attention: Nq (1..32) query rows against an Nk-row key/value cache

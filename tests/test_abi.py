@@ -9,13 +9,15 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa355.h")
+HEADER_UNFUSED = os.path.join(ROOT, "include", "fa355_unfused.h")
 LIB = os.path.join(ROOT, "exact_io_aware_12_amd", "libfa355.so")
+LIB_UNFUSED = os.path.join(ROOT, "exact_io_aware_12_amd", "libfa355_unfused.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libfa355.so not built")
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"FA355_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text)))
 
 
@@ -35,8 +37,8 @@ def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_kernel_name", "fa_bwd_noalloc",
                            "fa_bwd_workspace_bytes", "fa_decode_fwd",
                            "fa_decode_workspace_bytes", "fa_fa1_fwd", "fa_fa1_workspace_bytes",
-                           "fa_fwd", "fa_fwd_kernel_name", "fa_strerror", "fa_unfused_fwd",
-                           "fa_unfused_workspace_bytes"]
+                           "fa_fwd", "fa_fwd_kernel_name", "fa_strerror"]
+    assert _declared(HEADER_UNFUSED) == ["fa_unfused_fwd", "fa_unfused_workspace_bytes"]
 
 
 def test_fwd_kernel_name_follows_the_dispatch_rule(fa):
@@ -78,9 +80,26 @@ def test_bwd_kernel_name_follows_the_dispatch_rule(fa):
 
 def test_every_declared_symbol_is_exported():
     import torch  # noqa: F401  (torch's HIP runtime first, as the binding does)
-    lib = ctypes.CDLL(LIB)
-    for name in _declared():
-        assert hasattr(lib, name), name
+    for header, path in ((HEADER, LIB), (HEADER_UNFUSED, LIB_UNFUSED)):
+        lib = ctypes.CDLL(path)
+        for name in _declared(header):
+            assert hasattr(lib, name), (path, name)
+
+
+def _needed(path):
+    import subprocess
+    out = subprocess.run(["readelf", "-d", path], capture_output=True, text=True, check=True)
+    return re.findall(r"\(NEEDED\)\s+Shared library: \[([^\]]+)\]", out.stdout)
+
+
+def test_fused_library_does_not_depend_on_rocblas():
+    """libfa355.so needs the HIP runtime and the C/C++ runtimes only; rocBLAS
+    is a dependency of the unfused comparator's library alone."""
+    needed = _needed(LIB)
+    assert any(n.startswith("libamdhip64") for n in needed), needed
+    assert not any("rocblas" in n or "hipblas" in n for n in needed), needed
+    assert any("rocblas" in n for n in _needed(LIB_UNFUSED))
+    assert not any(n.startswith("libfa355") for n in _needed(LIB_UNFUSED))
 
 
 def test_codes_match_binding(fa):
@@ -160,6 +179,7 @@ def test_bwd_workspace(fa):
 @pytest.mark.parametrize("which", ["q", "dout", "lse", "dv"])
 def test_bwd_align(fa, which):
     assert _bwd(fa, **{which: GOOD + 4}) == fa.FA_ERR_ALIGN
+    assert _bwd(fa, ws=GOOD + 8) == fa.FA_ERR_ALIGN
 
 
 # ------------------------------------------------ fa_bwd_noalloc (static scratch)
@@ -194,7 +214,6 @@ def test_noalloc_validation(fa):
     assert _bwd_na(fa, N=0) == fa.FA_ERR_SHAPE
     assert _bwd_na(fa, scale=math.nan) == fa.FA_ERR_SCALE
     assert _bwd_na(fa, dk=GOOD + 2) == fa.FA_ERR_ALIGN
-    assert _bwd(fa, ws=GOOD + 8) == fa.FA_ERR_ALIGN
 
 
 def test_bwd_shape_and_scale(fa):
@@ -209,6 +228,14 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mod, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         mod.library()
+
+
+def test_unfused_binding_fails_loudly_without_its_library(monkeypatch, tmp_path):
+    from exact_io_aware_12_amd import fa as mod
+    monkeypatch.setattr(mod, "_lib_unfused", None)
+    monkeypatch.setattr(mod, "_LIB_UNFUSED_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        mod.library_unfused()
 
 
 def test_single_hip_runtime_mapped():
@@ -333,3 +360,35 @@ def test_decode_validation(fa):
     assert _dec(fa, Nk=0, ws_bytes=1 << 20) == fa.FA_ERR_SHAPE
     assert _dec(fa, d=80, ws_bytes=1 << 20) == fa.FA_ERR_HEADDIM
     assert _dec(fa, scale=math.inf) == fa.FA_ERR_SCALE
+
+
+# ---------------------------------------------------------------- sanitizers
+def test_entry_points_under_address_and_ub_sanitizers(tmp_path):
+    """The C entry points' host code (fa_api.cpp, fa_unfused_api.cpp) built by
+    g++ with -fsanitize=address,undefined against stand-in launchers
+    (tests/abi_host/stubs.cpp) and driven through valid and invalid calls
+    (tests/abi_host/driver.cpp): every argument reaches the launcher intact,
+    every invalid call is refused without a launch, and the sanitizers report
+    nothing. CPU only; no GPU code is built."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    csrc = os.path.join(ROOT, "exact_io_aware_12_amd", "csrc")
+    host = os.path.join(ROOT, "tests", "abi_host")
+    exe = str(tmp_path / "abi_sanitized")
+    cmd = [gxx, "-std=c++17", "-g", "-O1", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", os.path.join(csrc, "fa_api.cpp"),
+           os.path.join(csrc, "fa_unfused_api.cpp"), os.path.join(host, "stubs.cpp"),
+           os.path.join(host, "driver.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    # verify_asan_link_order=0: the environment may preload other libraries
+    # ahead of the sanitizer runtime; that is harmless for this program.
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0 and r.stdout.strip() == "ABI OK", r.stdout + r.stderr
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr
