@@ -30,6 +30,90 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s (bf16, d=128) and % of MI355X bf16 MFMA peak"
 
 
+# Child process that polls the GPU clock (amdsmi, per-XCD current gfxclk) every
+# ~0.3 ms until its stdin closes, then prints the samples as JSON. It is
+# started before this process touches the GPU and never touches it itself.
+_CLOCK_POLLER = r"""
+import json, select, sys, time
+try:
+    import amdsmi
+    amdsmi.amdsmi_init()
+    h = amdsmi.amdsmi_get_processor_handles()[0]
+except Exception as e:
+    print(json.dumps({"error": repr(e)}), flush=True)
+    sys.exit(0)
+print("ready", flush=True)
+samples = []
+while True:
+    r, _, _ = select.select([sys.stdin], [], [], 0)
+    if r:
+        break
+    try:
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        c = [x for x in m.get("current_gfxclks", []) if isinstance(x, (int, float))]
+        if not c and isinstance(m.get("current_gfxclk"), (int, float)):
+            c = [m["current_gfxclk"]]
+        if c:
+            samples.append((time.monotonic(), sum(c) / len(c)))
+    except Exception:
+        pass
+    time.sleep(0.0002)
+amdsmi.amdsmi_shut_down()
+print(json.dumps({"samples": samples}), flush=True)
+"""
+
+
+class ClockPoller:
+    """GPU shader-clock samples in named time windows (time.monotonic).
+
+    ``mark(name, t0, t1)`` records a window; ``finish()`` stops the poller and
+    returns {name: {"mean", "min", "max", "samples"}} for each window (None
+    when the clock cannot be read)."""
+
+    def __init__(self):
+        import subprocess
+        self.windows = []
+        self.proc = None
+        try:
+            self.proc = subprocess.Popen([sys.executable, "-c", _CLOCK_POLLER],
+                                         stdin=subprocess.PIPE, stdout=subprocess.PIPE,
+                                         stderr=subprocess.DEVNULL, text=True)
+            line = self.proc.stdout.readline().strip()
+            if line != "ready":
+                self.proc.wait(timeout=10)
+                self.proc = None
+        except Exception:
+            self.proc = None
+
+    def mark(self, name, t0, t1):
+        self.windows.append((name, t0, t1))
+
+    def finish(self):
+        if self.proc is None:
+            return {name: None for name, _, _ in self.windows}
+        try:
+            out, _ = self.proc.communicate(input="stop\n", timeout=30)
+            samples = json.loads(out.strip().splitlines()[-1]).get("samples", [])
+        except Exception:
+            return {name: None for name, _, _ in self.windows}
+        res = {}
+        for name, t0, t1 in self.windows:
+            xs = [c for t, c in samples if t0 <= t <= t1]
+            res[name] = ({"mean": round(sum(xs) / len(xs), 1), "min": min(xs), "max": max(xs),
+                          "samples": len(xs)} if xs else None)
+        return res
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -53,6 +137,10 @@ def parse():
     p.add_argument("--fa1", action="store_true",
                    help="also time the loop-order comparator (outer loop over key/value "
                         "tiles, one workgroup per head) on the same forward inputs")
+    p.add_argument("--oracle-all", action="store_true",
+                   help="instead of the GPU step, time the oracle (as it stands) on every "
+                        "workload in full on the host cores: median of 3 runs for workloads "
+                        "1-2, one run for 3-5; one JSON line")
     p.add_argument("--no-long-fwd", action="store_true",
                    help="skip the causal d=128 long-sequence forwards (workloads 3 and 4) "
                         "that the default fwd+bwd run also times")
@@ -91,7 +179,7 @@ def median(xs):
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
 
 
-def long_forwards(fa, torch, fi, dev, warmup=20, calls=50):
+def long_forwards(fa, torch, fi, dev, clock, warmup=20, calls=50):
     """The causal d=128 forwards at N >= 4096 (workloads 3 and 4), where the
     >= 50 %-of-peak forward target is stated: HIP-event times of `calls` calls
     on the launch stream after `warmup`, on the seeded inputs."""
@@ -108,11 +196,14 @@ def long_forwards(fa, torch, fi, dev, warmup=20, calls=50):
         for _ in range(warmup):
             fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(calls)]
+        torch.cuda.synchronize()
+        t0 = time.monotonic()
         for e in ev:
             e[0].record(stream)
             fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
             e[1].record(stream)
         torch.cuda.synchronize()
+        clock.mark(w.name, t0, time.monotonic())
         ms = [e[0].elapsed_time(e[1]) for e in ev]
         avg = sum(ms) / len(ms)
         tf = w.fwd_flops() / (avg * 1e-3) / 1e12
@@ -130,11 +221,7 @@ def cpu_baseline(w, inp, budget_s):
     import numpy as np
     import oracle
     from exact_io_aware_12_amd.inputs import bf16_bits_to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max(int(x.get("num_threads", 1)) for x in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = blas_threads()
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done, flops, t_total = 0, 0.0, 0.0
     per_head_fwd = w.fwd_flops() / len(heads)
@@ -151,15 +238,91 @@ def cpu_baseline(w, inp, budget_s):
         flops += per_head_fwd + per_head_bwd
         if t_total >= budget_s:
             break
-    return {
+    rec = {
         "value": flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} heads, {'fwd+bwd' if w.backward else 'fwd'} in fp64 "
-                  f"(numpy/OpenBLAS), {t_total:.1f} s",
+                  f"(numpy/OpenBLAS, one head at a time), {t_total:.1f} s",
         "seconds_per_step_extrapolated": t_total / done * len(heads),
+        "cpu_model": cpu_model(),
+        "host_cpus": len(os.sched_getaffinity(0)),
     }
+    if inp.q32 is not None:
+        rec["fp32_input_context"] = fp32_input_context(w, inp)
+    return rec
+
+
+def blas_threads() -> int:
+    """Threads the oracle's BLAS calls use (the threads it actually runs on)."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        if info:
+            return max(int(x.get("num_threads", 1)) for x in info)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def fp32_input_context(w, inp):
+    """How far the oracle's O and LSE move when it sees the fp32 draws instead
+    of their bf16 roundings (the inputs both sides are compared on): input
+    quantization, reported as context, not a parity figure."""
+    import numpy as np
+    import oracle
+    from exact_io_aware_12_amd.inputs import bf16_bits_to_f64
+    o32, l32 = oracle.attention_fwd(inp.q32.astype(np.float64), inp.k32.astype(np.float64),
+                                    inp.v32.astype(np.float64), w.scale, w.causal)
+    o16, l16 = oracle.attention_fwd(bf16_bits_to_f64(inp.q), bf16_bits_to_f64(inp.k),
+                                    bf16_bits_to_f64(inp.v), w.scale, w.causal)
+    return {"O_max_abs_shift": float(np.abs(o32 - o16).max()),
+            "LSE_max_abs_shift": float(np.abs(l32 - l16).max()),
+            "note": "oracle on the fp32 draws vs on their bf16 roundings"}
+
+
+def run_oracle_all(args):
+    """The oracle, as it stands, on every workload in full on the host cores:
+    median of 3 runs for the small workloads 1-2, one run for 3-5."""
+    import oracle
+    from exact_io_aware_12_amd import inputs as fi
+    from exact_io_aware_12_amd.inputs import bf16_bits_to_f64
+    out = []
+    for idx in (1, 2, 3, 4, 5):
+        w = fi.WORKLOADS[idx]
+        inp = fi.make_inputs(idx)
+        q, k, v = (bf16_bits_to_f64(x) for x in (inp.q, inp.k, inp.v))
+        do = bf16_bits_to_f64(inp.do) if w.backward else None
+        runs = 3 if idx <= 2 else 1
+        ts = []
+        for _ in range(runs):
+            # One head per call (the oracle loops over heads the same way);
+            # the sum of the calls' times is the run's time.
+            total, last = 0.0, time.perf_counter()
+            for b in range(w.B):
+                for h in range(w.H):
+                    t0 = time.perf_counter()
+                    oracle.attention_fwd(q[b, h], k[b, h], v[b, h], w.scale, w.causal)
+                    if w.backward:
+                        oracle.attention_bwd(q[b, h], k[b, h], v[b, h], do[b, h], w.scale,
+                                             w.causal)
+                    total += time.perf_counter() - t0
+                    if time.perf_counter() - last > 10:
+                        last = time.perf_counter()
+                        print(f"[oracle] {w.name}: head {b},{h}, {total:.1f} s so far",
+                              file=sys.stderr, flush=True)
+            ts.append(total)
+        sec = median(ts)
+        flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
+        out.append({"workload": w.name, "pass": "fwd+bwd" if w.backward else "fwd",
+                    "runs": runs, "seconds": round(sec, 4),
+                    "GFLOP_per_s": round(flops / sec / 1e9, 2)})
+        print(f"[oracle] {w.name}: {sec:.3f} s", file=sys.stderr, flush=True)
+    print(json.dumps({"oracle_times": out, "cores": blas_threads(),
+                      "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+                      "kind": "oracle", "note": "fp64 NumPy/OpenBLAS, heads one at a time, "
+                      "all heads of each workload"}), flush=True)
 
 
 def run_fwd_shape(args):
@@ -296,6 +459,9 @@ def main():
               f"Asked for --gpus {args.gpus} (WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
+    if args.oracle_all:
+        run_oracle_all(args)
+        return
     if args.decode is not None:
         run_decode(args)
         return
@@ -308,13 +474,14 @@ def main():
     from exact_io_aware_12_amd import fa
     from exact_io_aware_12_amd import inputs as fi
 
+    clock = ClockPoller()   # before anything touches the GPU
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     fa.library()
     dev = torch.device("cuda:0")
     w = fi.WORKLOADS[args.workload]
-    inp = fi.make_inputs(args.workload)
+    inp = fi.make_inputs(args.workload, keep_f32=(args.workload == 1))
 
     def gpu(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -348,10 +515,12 @@ def main():
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    m0 = time.monotonic()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock.mark("step", m0, time.monotonic())
 
     fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in events] if w.backward else [0.0] * args.steps
@@ -489,8 +658,22 @@ def main():
         rec["unfused"] = unfused
     if fa1 is not None:
         rec["fa1_order"] = fa1
+    if w.N * w.B * w.H <= 128:
+        # A single 128-row tile: one workgroup on 256 CUs, launch-latency
+        # bound; reported in microseconds with no fraction-of-peak claim.
+        rec["latency_us"] = {"avg": round(f_avg * 1e3, 2), "median": round(median(fwd_ms) * 1e3, 2),
+                             "min": round(min(fwd_ms) * 1e3, 2)}
+        rec["roofline"]["note"] = ("launch-latency bound (one workgroup); the fraction is not "
+                                   "a throughput claim")
     if w.backward and not args.no_long_fwd:
-        rec["fwd_causal_long"] = long_forwards(fa, torch, fi, dev)
+        rec["fwd_causal_long"] = long_forwards(fa, torch, fi, dev, clock)
+    clocks = clock.finish()
+    rec["sclk_mhz"] = dict(clocks.get("step") or {}, source="amdsmi current_gfxclks, mean "
+                           "of the 8 XCDs, polled every ~0.3 ms during the timed steps") \
+        if clocks.get("step") else None
+    for ent in rec.get("fwd_causal_long", []):
+        c = clocks.get(ent["workload"])
+        ent["sclk_mhz_mean"] = c["mean"] if c else None
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
