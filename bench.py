@@ -137,6 +137,10 @@ def parse():
     p.add_argument("--fa1", action="store_true",
                    help="also time the loop-order comparator (outer loop over key/value "
                         "tiles, one workgroup per head) on the same forward inputs")
+    p.add_argument("--persistent", action="store_true",
+                   help="also time the persistent-grid comparator (at most two resident "
+                        "workgroups per CU looping over the query tiles in a static snake "
+                        "order) on the same forward inputs")
     p.add_argument("--oracle-all", action="store_true",
                    help="instead of the GPU step, time the oracle (as it stands) on every "
                         "workload in full on the host cores: median of 3 runs for workloads "
@@ -619,6 +623,36 @@ def main():
                        "once per (key tile, query tile) pair"}
         del ws_1
 
+    persistent = None
+    if args.persistent:
+        o_p = torch.empty_like(q)
+        lse_p = torch.empty_like(lse)
+
+        def fwdp():
+            fa.fwd_persistent(q, k, v, causal=w.causal, scale=w.scale, out=o_p, lse=lse_p)
+
+        for _ in range(3):
+            fwdp()
+        torch.cuda.synchronize()
+        n_p = max(3, min(args.steps, 50))
+        # Back to back, as the fused forward's steps are timed.
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_p)]
+        for e in pev:
+            e[0].record(stream)
+            fwdp()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        pms = [e[0].elapsed_time(e[1]) for e in pev]
+        p_ms = sum(pms) / len(pms)
+        persistent = {"avg_ms": round(p_ms, 4), "median_ms": round(median(pms), 4),
+                      "calls": n_p,
+                      "fwd_tflops": round(w.fwd_flops() / (p_ms * 1e-3) / 1e12, 2),
+                      "fused_fwd_speedup": round(p_ms / f_avg, 3),
+                      "workgroups": min(512, ((w.N + 127) // 128) * w.B * w.H),
+                      "note": "128-row forward kernel on a persistent grid, static snake order "
+                              "within each XCD's heads; fa_fwd launches one workgroup per query "
+                              "tile and its kernel is named in roofline.kernel"}
+
     if args.copy_calib_mib > 0:
         src = torch.empty(args.copy_calib_mib * 2 ** 20, device=dev, dtype=torch.uint8)
         dst = torch.empty_like(src)
@@ -658,6 +692,8 @@ def main():
         rec["unfused"] = unfused
     if fa1 is not None:
         rec["fa1_order"] = fa1
+    if persistent is not None:
+        rec["persistent"] = persistent
     if w.N * w.B * w.H <= 128:
         # A single 128-row tile: one workgroup on 256 CUs, launch-latency
         # bound; reported in microseconds with no fraction-of-peak claim.

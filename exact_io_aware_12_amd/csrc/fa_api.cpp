@@ -13,6 +13,9 @@ namespace fa {
 hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* o, float* lse, int BH, int N, int d, float scale,
                         bool causal, hipStream_t stream);
+hipError_t fwd_persistent_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* o, float* lse, int BH, int N, int d, float scale,
+                                   bool causal, hipStream_t stream);
 bool fwd_uses_two_group_kernel(int BH, int N, int d, bool causal);
 bool fwd_uses_split_kernel(int BH, int N, int d);
 bool fwd_uses_split_groups(int BH, int N, int d);
@@ -49,6 +52,21 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   hipError_t e = fa::fwd_dispatch(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B * H, N, d, scale,
+      causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int N, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int rc = check_shape(B, H, N, d);
+  if (rc != FA_OK) return rc;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  hipError_t e = fa::fwd_persistent_dispatch(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B * H, N, d, scale,
       causal != 0, static_cast<hipStream_t>(stream));

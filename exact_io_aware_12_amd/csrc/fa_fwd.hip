@@ -216,22 +216,32 @@ __device__ __forceinline__ void wait_dma() {
 // scaled value is -inf as well) and every tile uses exp2(fma(s, c2, -m)).
 // Otherwise (scale <= 0, rare) every tile is scaled first and uses
 // exp2(s - m).
+// Item b (a workgroup, or an item of the persistent kernel) -> (head, query
+// tile rank; rank 0 = heaviest causal tile).
+__device__ __forceinline__ void item_to_tile(int b, int BH, int xcd_group, int& head, int& rank) {
+  if (xcd_group > 0) {
+    // Workgroups are dispatched round-robin over the 8 XCDs; give XCD x the
+    // heads [x*G, (x+1)*G) so their K/V stay in that XCD's L2.
+    const int x = b & 7, s = b >> 3;
+    head = x * xcd_group + s % xcd_group;
+    rank = s / xcd_group;
+  } else {
+    head = b % BH;
+    rank = b / BH;
+  }
+}
+
+// One 128-row query tile (`rank`-th heaviest of head `head`): the whole
+// online-softmax pass and its epilogue, on the four LDS buffers given (each
+// G * TILE_BYTES bytes). Called once per workgroup by fa_fwd_kernel and once
+// per item by the persistent comparator kernel.
 template <int D, bool CAUSAL, bool POS, int G>
-__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
+__device__ __forceinline__ void fwd_tile(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, int BH, int N, int ntq, float c2, int xcd_group) {
+    float* __restrict__ LSE, int N, int ntq, float c2, int head, int rank, int tid,
+    uint8_t* k_lds0, uint8_t* k_lds1, uint8_t* v_lds0, uint8_t* v_lds1) {
   using C = FwdCfg<D>;
-  // Four distinct LDS objects (not one indexed array): the loop below is
-  // unrolled by two so each access names its buffer statically, which lets
-  // the compiler see that an in-flight DMA into one buffer does not alias
-  // the reads of another (otherwise it waits for the DMA before every read).
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[G * C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[G * C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[G * C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[G * C::TILE_BYTES];
-
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wall = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   // G = 2: two groups of 4 waves own the same 128 rows; group g takes the key
@@ -242,21 +252,6 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int gofs = grp * C::TILE_BYTES;   // this group's half of each buffer
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // Workgroup -> (head, query tile).
-  int head, rank;
-  {
-    const int b = blockIdx.x;
-    if (xcd_group > 0) {
-      // Workgroups are dispatched round-robin over the 8 XCDs; give XCD x the
-      // heads [x*G, (x+1)*G) so their K/V stay in that XCD's L2.
-      const int x = b & 7, s = b >> 3;
-      head = x * xcd_group + s % xcd_group;
-      rank = s / xcd_group;
-    } else {
-      head = b % BH;
-      rank = b / BH;
-    }
-  }
   const int qt = CAUSAL ? (ntq - 1 - rank) : rank;
   const int q0 = qt * C::BM;
   const int qw = q0 + w * 32;          // first query row of this wave
@@ -558,6 +553,112 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
                          ov, lane);
   }
   if (qrow < N && hi == 0) LSE[(size_t)head * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+}
+
+template <int D, bool CAUSAL, bool POS, int G>
+__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, int BH, int N, int ntq, float c2, int xcd_group) {
+  using C = FwdCfg<D>;
+  // Four distinct LDS objects (not one indexed array): the loop below is
+  // unrolled by two so each access names its buffer statically, which lets
+  // the compiler see that an in-flight DMA into one buffer does not alias
+  // the reads of another (otherwise it waits for the DMA before every read).
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[G * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[G * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[G * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[G * C::TILE_BYTES];
+
+  // Workgroup -> (head, query tile).
+  int head, rank;
+  item_to_tile(blockIdx.x, BH, xcd_group, head, rank);
+  fwd_tile<D, CAUSAL, POS, G>(Q, K, V, O, LSE, N, ntq, c2, head, rank, threadIdx.x, k_lds0,
+                              k_lds1, v_lds0, v_lds1);
+}
+
+// Comparator: the same forward pass on a persistent grid. At most two 4-wave
+// workgroups per CU (512) stay resident and each loops over query tiles
+// ("items", the workgroups of fa_fwd_kernel in its heaviest-first order).
+// The schedule is static: within the items of each XCD, round k gives
+// workgroup g the k-th block of items in "snake" order (g in even rounds,
+// the mirror position in odd ones), so a workgroup that draws a heavy
+// causal tile in one round draws a light one in the next. fa_fwd_kernel
+// instead leaves the balancing to the hardware dispatcher, which starts each
+// next workgroup on whichever slot frees first. The loop state (round, item)
+// is uniform and lives in scalar registers.
+template <int D, bool CAUSAL, bool POS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_persistent_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, int BH, int N, int ntq, float c2, int xcd_group) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[C::TILE_BYTES];
+  const int total = ntq * BH;
+  // Items of one XCD (b = 8s + x) when the heads are grouped by XCD, else
+  // all items (b = s); P workgroups share them, PL per XCD.
+  const int groups = xcd_group > 0 ? 8 : 1;
+  const int g = blockIdx.x;
+  const int x = g % groups, gl = g / groups;
+  const int PL = gridDim.x / groups, TL = total / groups;
+  for (int k = 0;; ++k) {
+    const int s = k * PL + ((k & 1) ? PL - 1 - gl : gl);
+    if (s >= TL) break;   // s grows with k for every workgroup
+    if (k > 0) __syncthreads();   // the previous item's LDS reads and stores are done
+    int head, rank;
+    item_to_tile(s * groups + x, BH, xcd_group, head, rank);
+    // The thread id, the pointers and the sizes pass through empty asm
+    // statements: everything derived from them is then recomputed per item
+    // rather than hoisted out of the loop and held in registers across it.
+    int tid = threadIdx.x, n = N, nq = ntq;
+    float c = c2;
+    const uint16_t *q = Q, *kk = K, *vv = V;
+    uint16_t* o = O;
+    float* lse = LSE;
+    asm volatile("" : "+v"(tid));
+    asm volatile("" : "+s"(n), "+s"(nq), "+s"(c), "+s"(q), "+s"(kk), "+s"(vv), "+s"(o), "+s"(lse));
+    fwd_tile<D, CAUSAL, POS, 1>(q, kk, vv, o, lse, n, nq, c, head, rank, tid, k_lds0, k_lds1,
+                                v_lds0, v_lds1);
+  }
+}
+
+template <int D, bool CAUSAL, bool POS>
+static hipError_t launch_fwd_persistent(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        uint16_t* o, float* lse, int BH, int N, float scale,
+                                        hipStream_t stream) {
+  using C = FwdCfg<D>;
+  const int ntq = (N + C::BM - 1) / C::BM;
+  const int xcd_group = (BH % 8 == 0) ? BH / 8 : 0;
+  const float c2 = scale * kLog2e;
+  // Two resident workgroups per CU on 256 CUs (a multiple of 8, so that
+  // workgroup g runs on XCD g % 8), or one per item if there are fewer.
+  const int total = ntq * BH;
+  const int nwg = total < 512 ? total : 512;
+  hipLaunchKernelGGL((fa_fwd_persistent_kernel<D, CAUSAL, POS>), dim3((unsigned)nwg),
+                     dim3(C::THREADS), 0, stream, q, k, v, o, lse, BH, N, ntq, c2, xcd_group);
+  return hipGetLastError();
+}
+
+hipError_t fwd_persistent_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* o, float* lse, int BH, int N, int d, float scale,
+                                   bool causal, hipStream_t stream) {
+  const bool pos = scale > 0.f;
+#define FA_FWDP_CASE(DD, CC, PP) \
+  if (d == DD && causal == CC && pos == PP) \
+    return launch_fwd_persistent<DD, CC, PP>(q, k, v, o, lse, BH, N, scale, stream);
+  FA_FWDP_CASE(128, true, true)
+  FA_FWDP_CASE(128, false, true)
+  FA_FWDP_CASE(64, true, true)
+  FA_FWDP_CASE(64, false, true)
+  FA_FWDP_CASE(128, true, false)
+  FA_FWDP_CASE(128, false, false)
+  FA_FWDP_CASE(64, true, false)
+  FA_FWDP_CASE(64, false, false)
+#undef FA_FWDP_CASE
+  return hipErrorInvalidValue;
 }
 
 // d = 64 grids of at most 256 128-row query tiles (one per CU) with at least

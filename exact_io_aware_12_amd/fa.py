@@ -7,13 +7,15 @@ the C ABI, and every step of the computation runs in the library's kernels.
 PyTorch only supplies device memory and the stream. There is no fallback: if
 the library cannot be loaded, every call raises.
 
-The functions ``fa_fwd``, ``fa_fwd_kernel_name``, ``fa_bwd``, ``fa_bwd_noalloc``,
+The functions ``fa_fwd``, ``fa_fwd_persistent``, ``fa_fwd_kernel_name``, ``fa_bwd``,
+``fa_bwd_noalloc``,
 ``fa_bwd_kernel_name``, ``fa_bwd_workspace_bytes``,
 ``fa_unfused_fwd``, ``fa_unfused_workspace_bytes``, ``fa_fa1_fwd``,
 ``fa_fa1_workspace_bytes``, ``fa_decode_fwd``,
 ``fa_decode_workspace_bytes`` and ``fa_strerror`` are the raw C entry points
 (ctypes). ``fwd`` / ``bwd`` / ``unfused_fwd`` / ``fa1_fwd`` / ``decode_fwd`` are
-tensor-level wrappers with the same semantics.
+tensor-level wrappers with the same semantics (``fwd_persistent`` for the
+persistent comparator).
 """
 from __future__ import annotations
 
@@ -60,6 +62,8 @@ def _load():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_persistent.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd_persistent.restype = i
     lib.fa_fwd_kernel_name.argtypes = [i, i, i, i, i]
     lib.fa_fwd_kernel_name.restype = ctypes.c_char_p
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
@@ -118,6 +122,10 @@ def library_unfused():
 # ----------------------------------------------------------------- raw C ABI
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
     return _load().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, int(causal), stream)
+
+
+def fa_fwd_persistent(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
+    return _load().fa_fwd_persistent(q, k, v, o, lse, B, H, N, d, scale, int(causal), stream)
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
@@ -213,6 +221,19 @@ def _stream_ptr(device, stream=None):
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
         stream=None):
     """O, LSE = attention(q, k, v): bf16 [B,H,N,d] in, bf16 O and fp32 LSE out."""
+    return _fwd_call(fa_fwd, "fa_fwd", q, k, v, causal, scale, out, lse, stream)
+
+
+def fwd_persistent(q, k, v, *, causal: bool = False, scale: float | None = None, out=None,
+                   lse=None, stream=None):
+    """The same O, LSE as ``fwd`` on a persistent grid (at most two resident
+    workgroups per CU looping over the query tiles in a static snake order):
+    the measured scheduling comparator of the fused pass."""
+    return _fwd_call(fa_fwd_persistent, "fa_fwd_persistent", q, k, v, causal, scale, out, lse,
+                     stream)
+
+
+def _fwd_call(raw, name, q, k, v, causal, scale, out, lse, stream):
     import torch
     _check(q, "q", dtype=torch.bfloat16)
     if q.dim() != 4:
@@ -228,10 +249,10 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
         lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
     _check(out, "out", q.shape, torch.bfloat16)
     _check(lse, "lse", (B, H, N), torch.float32)
-    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                B, H, N, d, float(scale), causal, _stream_ptr(q.device, stream))
+    rc = raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+             B, H, N, d, float(scale), causal, _stream_ptr(q.device, stream))
     if rc != FA_OK:
-        raise FAError(rc, "fa_fwd")
+        raise FAError(rc, name)
     return out, lse
 
 

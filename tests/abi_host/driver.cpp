@@ -42,9 +42,17 @@ int main() {
   CHECK(fa_fwd(P(A), P(A), P(A), P(A), lse, 1, 1, 16, 96, 1.f, 0, s) == FA_ERR_HEADDIM);
   CHECK(fa_fwd(P(A), P(A), P(A), P(A), lse, 1, 1, 16, 64, NAN, 0, s) == FA_ERR_SCALE);
   CHECK(fa_fwd(P(A), P(A + 8), P(A), P(A), lse, 1, 1, 16, 64, 1.f, 0, s) == FA_ERR_ALIGN);
+  CHECK(fa_fwd_persistent(P(A), P(A), P(A), P(A), lse, 4, 8, 300, 64, -0.5f, 0, s) == FA_OK);
+  CHECK(saw("fwd_persistent", 32, 300, 64, -0.5f, false));
+  CHECK(fa_fwd_persistent(P(A), P(A), P(A), nullptr, lse, 1, 1, 16, 64, 1.f, 0, s) == FA_ERR_NULL);
+  CHECK(fa_fwd_persistent(P(A), P(A), P(A), P(A), lse, 1, 1, 16, 80, 1.f, 0, s) == FA_ERR_HEADDIM);
+  CHECK(fa_fwd_persistent(P(A), P(A), P(A), P(A), lse, 1, 1, 16, 64, INFINITY, 0, s) ==
+        FA_ERR_SCALE);
+  CHECK(fa_fwd_persistent(P(A), P(A), P(A + 4), P(A), lse, 1, 1, 16, 64, 1.f, 0, s) ==
+        FA_ERR_ALIGN);
   CHECK(fa_fwd_kernel_name(1, 1, 16, 64, 0) != nullptr);
   CHECK(fa_fwd_kernel_name(1, 1, 16, 65, 0) == nullptr);
-  const int calls_after_fwd = g_last.calls;
+  const int calls_after_fwd = g_last.calls;   // fa_fwd and fa_fwd_persistent
 
   // ---- fa_bwd (+ workspace), fa_bwd_noalloc, fa_bwd_kernel_name
   const size_t ws = fa_bwd_workspace_bytes(2, 16, 2048, 128);
@@ -99,8 +107,8 @@ int main() {
         FA_ERR_SCALE);
 
   // ---- every invalid call above launched nothing
-  CHECK(calls_after_fwd == 1);
-  CHECK(g_last.calls == 6);
+  CHECK(calls_after_fwd == 2);
+  CHECK(g_last.calls == 7);
 
   // ---- fa_strerror covers every code
   for (int c = 0; c <= 9; ++c) CHECK(strcmp(fa_strerror(c), "unknown fa355 error code") != 0);

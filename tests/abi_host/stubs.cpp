@@ -30,6 +30,12 @@ hipError_t fwd_dispatch(const uint16_t*, const uint16_t*, const uint16_t*, uint1
   record("fwd", BH, N, d, scale, causal, nullptr, stream);
   return hipSuccess;
 }
+hipError_t fwd_persistent_dispatch(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*,
+                                   float*, int BH, int N, int d, float scale, bool causal,
+                                   hipStream_t stream) {
+  record("fwd_persistent", BH, N, d, scale, causal, nullptr, stream);
+  return hipSuccess;
+}
 bool fwd_uses_two_group_kernel(int, int N, int d, bool) { return d == 128 && N >= 8192; }
 bool fwd_uses_split_kernel(int, int, int) { return false; }
 bool fwd_uses_split_groups(int, int, int) { return false; }

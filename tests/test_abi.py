@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_kernel_name", "fa_bwd_noalloc",
                            "fa_bwd_workspace_bytes", "fa_decode_fwd",
                            "fa_decode_workspace_bytes", "fa_fa1_fwd", "fa_fa1_workspace_bytes",
-                           "fa_fwd", "fa_fwd_kernel_name", "fa_strerror"]
+                           "fa_fwd", "fa_fwd_kernel_name", "fa_fwd_persistent", "fa_strerror"]
     assert _declared(HEADER_UNFUSED) == ["fa_unfused_fwd", "fa_unfused_workspace_bytes"]
 
 
@@ -144,6 +144,17 @@ def test_fwd_scale(fa, scale):
 @pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
 def test_fwd_align(fa, which):
     assert _fwd(fa, **{which: GOOD + 8}) == fa.FA_ERR_ALIGN
+
+
+def test_fwd_persistent_validation(fa):
+    def call(q=GOOD, o=GOOD, B=1, N=16, d=64, scale=0.125):
+        return fa.fa_fwd_persistent(q, GOOD, GOOD, o, GOOD, B, 1, N, d, scale, 1, None)
+    assert call(q=None) == fa.FA_ERR_NULL
+    assert call(N=0) == fa.FA_ERR_SHAPE
+    assert call(B=1 << 20, N=1 << 12) == fa.FA_ERR_SHAPE
+    assert call(d=96) == fa.FA_ERR_HEADDIM
+    assert call(scale=math.nan) == fa.FA_ERR_SCALE
+    assert call(o=GOOD + 2) == fa.FA_ERR_ALIGN
 
 
 def test_workspace_bytes(fa):
