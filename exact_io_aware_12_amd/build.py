@@ -19,6 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa355.so")
 # The unfused comparator: its own library, the only one linked with rocBLAS.
 LIB_UNFUSED = os.path.join(PKG, "libfa355_unfused.so")
+# The race-check build of libfa355.so (FA_STRICT_SYNC: every global -> LDS
+# copy awaited as soon as it is issued), compared bit for bit with the normal
+# build by the GPU tests.
+LIB_STRICT = os.path.join(PKG, "libfa355_strict.so")
 # Calibration program (unit ceilings measured on the device), not linked into
 # the library.
 CEILINGS = os.path.join(PKG, "fa355_ceilings")
@@ -35,6 +39,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-fvi
 
 def _compile(src: str, obj: str, extra: list[str]) -> None:
     cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    if obj.endswith(".strict.o"):
+        cmd.insert(-4, "-DFA_STRICT_SYNC")
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -55,11 +61,13 @@ def build(extra: list[str] | None = None) -> str:
     extra = list(extra or [])
     tmp = tempfile.mkdtemp(prefix="fa355_build_")
     try:
-        srcs = SOURCES + SOURCES_UNFUSED
-        objs = {s: os.path.join(tmp, s + ".o") for s in srcs}
-        with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-            list(ex.map(lambda s: _compile(s, objs[s], extra), srcs))
+        jobs = [(s, os.path.join(tmp, s + ".o")) for s in SOURCES + SOURCES_UNFUSED]
+        jobs += [(s, os.path.join(tmp, s + ".strict.o")) for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+            list(ex.map(lambda j: _compile(j[0], j[1], extra), jobs))
+        objs = dict(jobs[:len(SOURCES) + len(SOURCES_UNFUSED)])
         _link([objs[s] for s in SOURCES], LIB, [])
+        _link([os.path.join(tmp, s + ".strict.o") for s in SOURCES], LIB_STRICT, [])
         # rocBLAS serves the two plain GEMMs of the unfused comparator only.
         _link([objs[s] for s in SOURCES_UNFUSED], LIB_UNFUSED, ["-L/opt/rocm/lib", "-lrocblas"])
         cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, os.path.join(CSRC, "ceilings.hip"), "-o",

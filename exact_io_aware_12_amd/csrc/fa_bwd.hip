@@ -118,12 +118,14 @@ __device__ __forceinline__ int sw_off(int row, int col) {
 __device__ __forceinline__ void lds_copy16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(lds_addr) : "memory", "m0");
+  strict_copy_wait();
 }
 // Scalar-base form: the tile's base address is one SGPR pair and each lane
 // adds a 32-bit byte offset (no per-lane 64-bit address arithmetic).
 __device__ __forceinline__ void lds_copy16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+  strict_copy_wait();
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

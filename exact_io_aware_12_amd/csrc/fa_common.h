@@ -41,6 +41,19 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// Race-check build (-DFA_STRICT_SYNC, built as libfa355_strict.so): the wave
+// that issues a global -> LDS copy waits for it right away, so no copy is
+// ever in flight while the wave or its workgroup goes on. The normal build
+// overlaps the copies with MFMA work and relies on its barriers to keep every
+// read of a buffer away from a copy into it. Both builds compute the same
+// arithmetic in the same order: any difference in their outputs would be a
+// copy that raced with a read.
+__device__ __forceinline__ void strict_copy_wait() {
+#ifdef FA_STRICT_SYNC
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // s_waitcnt vmcnt(0)
+#endif
+}
+
 // NaN-propagating max / min (v_maximum3_f32 / v_minimum3_f32 on gfx950; no
 // operand canonicalisation as fmaxf needs in IEEE mode).
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }

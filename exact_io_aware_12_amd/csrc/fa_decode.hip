@@ -71,6 +71,7 @@ __device__ __forceinline__ int dv_src(int c, int lane, int& row) {
 __device__ __forceinline__ void dcopy16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+  strict_copy_wait();
 }
 #pragma clang diagnostic pop
 

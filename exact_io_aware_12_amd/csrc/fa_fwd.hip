@@ -138,6 +138,7 @@ __device__ __forceinline__ float tile_sum(const f32x16 (&s)[NB]) {
 __device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+  strict_copy_wait();
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {

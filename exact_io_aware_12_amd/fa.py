@@ -58,7 +58,18 @@ def _load():
         import torch  # noqa: F401
     except ImportError:
         pass
-    lib = ctypes.CDLL(_LIB_PATH)
+    _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def load_build(path: str):
+    """Another build of libfa355.so (for instance the race-check build
+    libfa355_strict.so next to it), with the same C signatures."""
+    _load()   # torch's HIP runtime and the main library first
+    return _bind(ctypes.CDLL(path))
+
+
+def _bind(lib):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_fwd.restype = i
@@ -84,7 +95,6 @@ def _load():
     lib.fa_decode_fwd.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 
