@@ -539,6 +539,17 @@ def main():
     cold_fwd_ms = cold[0].elapsed_time(cold[1])
     cold_bwd_ms = cold[1].elapsed_time(cold[2]) if w.backward else None
     del flush
+
+    # The SMU's clock reading lags the load by up to about a second, so a
+    # timed loop of a few tens of ms reads the idle level. The clock is
+    # therefore sampled over the second half of a 1 s untimed run of the same
+    # step right after the timed loop.
+    s0 = time.monotonic()
+    while time.monotonic() - s0 < 1.0:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    clock.mark("step_soak", s0 + 0.5, time.monotonic())
     ms_step = wall * 1e3 / args.steps
     flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
     value = flops / (ms_step * 1e-3) / 1e12
@@ -704,9 +715,13 @@ def main():
     if w.backward and not args.no_long_fwd:
         rec["fwd_causal_long"] = long_forwards(fa, torch, fi, dev, clock)
     clocks = clock.finish()
-    rec["sclk_mhz"] = dict(clocks.get("step") or {}, source="amdsmi current_gfxclks, mean "
-                           "of the 8 XCDs, polled every ~0.3 ms during the timed steps") \
-        if clocks.get("step") else None
+    rec["sclk_mhz"] = dict(clocks.get("step_soak") or {}, source=(
+        "amdsmi current_gfxclks (the SMU's clock level), mean of the 8 XCDs, polled every "
+        "~0.5 ms over the second half of a 1 s untimed run of the same step right after the "
+        "timed loop; the reading lags the load, and during the timed loop itself it showed "
+        f"{(clocks.get('step') or {}).get('mean')} MHz. Not the effective shader clock, which "
+        "GRBM_GUI_ACTIVE counters put lower under load (profiles/fa_kernels_clock_under_load.md)")) \
+        if clocks.get("step_soak") else None
     for ent in rec.get("fwd_causal_long", []):
         c = clocks.get(ent["workload"])
         ent["sclk_mhz_mean"] = c["mean"] if c else None

@@ -18,6 +18,14 @@
 //   ldsmfma MFMAs whose A operand comes from LDS, as the attention kernels
 //          read K (ds_read_b128) or V^T (two ds_read_b64_tr_b16), each read
 //          feeding one or two MFMAs; the reads run half an iteration ahead
+//   full   the forward's steady-state mix: each ds_read_b128 operand feeds R
+//          MFMAs, and every MFMA carries one softmax element's VALU work
+//          (fma, exp2, add to a row sum, and a bf16 pack every second
+//          element), placed after it by scheduling-group barriers. R = 1 at
+//          two waves per SIMD is the shape of the kernels (32 rows per
+//          wave); R = 2 at one wave per SIMD is a 64-row-per-wave design
+//          (twice the output registers, so one wave per SIMD), which halves
+//          the LDS bytes per MFMA
 //
 // Each is timed with HIP events at one and two 4-wave workgroups per CU (one
 // and two waves per SIMD), on 256 x {1,2} workgroups. Every kernel writes one
@@ -32,6 +40,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define CHECK(x)                                                                  \
   do {                                                                            \
@@ -227,6 +237,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+template <int R, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k_full(float* out, int iters, float cc) {
+  __shared__ __attribute__((aligned(1024))) unsigned char buf[32768];
+  for (int i = threadIdx.x; i < 32768 / 4; i += 256) reinterpret_cast<unsigned*>(buf)[i] = i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  bf16x8 b[R];
+  for (int r = 0; r < R; ++r) for (int i = 0; i < 8; ++i) b[r][i] = (__bf16)((i + r) * 0.01f);
+  f32x16 c[4 * R];
+  for (int i = 0; i < 4 * R; ++i) for (int j = 0; j < 16; ++j) c[i][j] = 0.f;
+  float x[16], rs[4] = {0.f, 0.f, 0.f, 0.f};
+  unsigned pk[8] = {};
+  for (int i = 0; i < 16; ++i) x[i] = -0.001f * (threadIdx.x + i);
+  // The K pattern of k_ldsmfma: operand i of a 16 KiB half, all < 32 KiB.
+  auto addr = [&](int i, int half) -> int {
+    const int kb = i & 1, ks = i >> 1;
+    return half * 16384 + (kb * 32 + l32) * 256 + (((2 * ks + hi) ^ (l32 & 15)) << 4);
+  };
+  auto rd = [&](int a) -> bf16x8 { return *reinterpret_cast<const bf16x8*>(buf + a); };
+  bf16x8 a0[8], a1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a0[i] = rd(addr(i, 0));
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (h == 0) a1[i] = rd(addr(8 + i, it & 1));
+        else a0[i] = rd(addr(i, (it + 1) & 1));
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          c[(i & 3) * R + r] = mfma(h == 0 ? a0[i] : a1[i], b[r], c[(i & 3) * R + r]);
+          const int k = (i * R + r) & 15;
+          const float e = __builtin_amdgcn_exp2f(fmaf(x[k], cc, -1.0f));
+          rs[k & 3] += e;
+          if (k & 1) {
+            f32x2 f = {x[k - 1], e};
+            pk[(k >> 1) & 7] ^= __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+          }
+          x[k] = e;
+        }
+      }
+      // Per operand: its read, then per MFMA the MFMA and 3-4 VALU /
+      // transcendental instructions.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+        }
+      }
+    }
+  }
+  float s = 0.f;
+  for (int i = 0; i < 4 * R; ++i) for (int j = 0; j < 16; ++j) s += c[i][j];
+  for (int i = 0; i < 8; ++i) s += (float)a0[i][0] + (float)pk[i];
+  for (int i = 0; i < 4; ++i) s += rs[i];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // Milliseconds of one launch after a short warm-up launch.
 template <typename F>
 static int timed(F launch, hipEvent_t e0, hipEvent_t e1, float* ms) {
@@ -295,6 +367,20 @@ int main() {
     printf("| mfma, A operand from LDS (%s), %d MFMA per operand | %d | %.1f TFLOP/s | %.0f FLOP |\n", TR ? "2 x ds_read_b64_tr_b16" : "ds_read_b128", R, wpc, R * fl16 / ms / 1e9, R * fl16 / (ms * 1e-3) / 256 / clk);
     FA_LDSMFMA(1, false) FA_LDSMFMA(2, false) FA_LDSMFMA(1, true) FA_LDSMFMA(2, true)
 #undef FA_LDSMFMA
+  }
+  // The forward's mix at its two candidate shapes, each at the occupancy its
+  // registers allow (256 x WPE workgroups of 4 waves).
+  {
+    const int it = 5000;
+    float ms = 0.f;
+#define FA_FULL(R, WPE)                                                                             \
+    if (timed([&](bool w) { hipLaunchKernelGGL((k_full<R, WPE>), dim3(256 * WPE), dim3(256), 0, 0, out, w ? 50 : it, 0.5f); }, e0, e1, &ms)) return 1; \
+    {                                                                                               \
+      const double fl = 256.0 * WPE * 4 * it * 16 * R * 32768.0;                                    \
+      printf("| mfma + softmax VALU per MFMA, LDS operand feeding %d MFMA(s) | %d | %.1f TFLOP/s | %.0f FLOP |\n", R, WPE, fl / ms / 1e9, fl / (ms * 1e-3) / 256 / clk); \
+    }
+    FA_FULL(1, 2) FA_FULL(2, 1) FA_FULL(1, 1) FA_FULL(2, 2)
+#undef FA_FULL
   }
   CHECK(hipFree(out));
   return 0;
