@@ -121,6 +121,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-clock-soak", action="store_true",
+                   help="skip the untimed runs after each timed loop that let the SMU's clock "
+                        "reading settle (for profiler runs: the trace then holds only the "
+                        "warm-up, timed and cold calls; sclk fields become null)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle sample")
     p.add_argument("--copy-calib-mib", type=int, default=0,
@@ -183,7 +187,21 @@ def median(xs):
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
 
 
-def long_forwards(fa, torch, fi, dev, clock, warmup=20, calls=50):
+def clock_soak(clock, name, fn, torch, seconds):
+    """Run `fn` back to back, untimed, for `seconds` and mark the last half as
+    window `name`. The SMU's clock reading (amdsmi) lags the load by up to about
+    a second and updates in steps, so a timed loop of a few tens of ms reads
+    the level of whatever ran before it; the soak gives it time to settle on
+    the clock this work runs at."""
+    s0 = time.monotonic()
+    while time.monotonic() - s0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    clock.mark(name, s0 + seconds / 2, time.monotonic())
+
+
+def long_forwards(fa, torch, fi, dev, clock, soak, warmup=20, calls=50):
     """The causal d=128 forwards at N >= 4096 (workloads 3 and 4), where the
     >= 50 %-of-peak forward target is stated: HIP-event times of `calls` calls
     on the launch stream after `warmup`, on the seeded inputs."""
@@ -207,7 +225,9 @@ def long_forwards(fa, torch, fi, dev, clock, warmup=20, calls=50):
             fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
             e[1].record(stream)
         torch.cuda.synchronize()
-        clock.mark(w.name, t0, time.monotonic())
+        if soak:
+            clock_soak(clock, w.name, lambda: fa.fwd(q, k, v, causal=w.causal, scale=w.scale,
+                                                     out=o, lse=lse), torch, 2.0)
         ms = [e[0].elapsed_time(e[1]) for e in ev]
         avg = sum(ms) / len(ms)
         tf = w.fwd_flops() / (avg * 1e-3) / 1e12
@@ -540,16 +560,8 @@ def main():
     cold_bwd_ms = cold[1].elapsed_time(cold[2]) if w.backward else None
     del flush
 
-    # The SMU's clock reading lags the load by up to about a second, so a
-    # timed loop of a few tens of ms reads the idle level. The clock is
-    # therefore sampled over the second half of a 1 s untimed run of the same
-    # step right after the timed loop.
-    s0 = time.monotonic()
-    while time.monotonic() - s0 < 1.0:
-        for _ in range(10):
-            step()
-        torch.cuda.synchronize()
-    clock.mark("step_soak", s0 + 0.5, time.monotonic())
+    if not args.no_clock_soak:
+        clock_soak(clock, "step_soak", step, torch, 3.0)
     ms_step = wall * 1e3 / args.steps
     flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
     value = flops / (ms_step * 1e-3) / 1e12
@@ -713,14 +725,14 @@ def main():
         rec["roofline"]["note"] = ("launch-latency bound (one workgroup); the fraction is not "
                                    "a throughput claim")
     if w.backward and not args.no_long_fwd:
-        rec["fwd_causal_long"] = long_forwards(fa, torch, fi, dev, clock)
+        rec["fwd_causal_long"] = long_forwards(fa, torch, fi, dev, clock, not args.no_clock_soak)
     clocks = clock.finish()
     rec["sclk_mhz"] = dict(clocks.get("step_soak") or {}, source=(
-        "amdsmi current_gfxclks (the SMU's clock level), mean of the 8 XCDs, polled every "
-        "~0.5 ms over the second half of a 1 s untimed run of the same step right after the "
-        "timed loop; the reading lags the load, and during the timed loop itself it showed "
-        f"{(clocks.get('step') or {}).get('mean')} MHz. Not the effective shader clock, which "
-        "GRBM_GUI_ACTIVE counters put lower under load (profiles/fa_kernels_clock_under_load.md)")) \
+        "amdsmi current_gfxclks (the SMU's clock reading), mean of the 8 XCDs, polled every "
+        "~0.5 ms over the last 1.5 s of a 3 s untimed run of the same step right after the "
+        "timed loop: the reading lags the load by up to about a second (during the timed loop "
+        f"itself it showed {(clocks.get('step') or {}).get('mean')} MHz). The counter-based "
+        "clock (GRBM_GUI_ACTIVE per dispatch) is in profiles/fa_kernels_clock_under_load.md")) \
         if clocks.get("step_soak") else None
     for ent in rec.get("fwd_causal_long", []):
         c = clocks.get(ent["workload"])
