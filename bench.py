@@ -10,7 +10,8 @@ forwards are 3 and 4).
 Prints ONE JSON line. ``value`` is algorithmic TFLOP/s over the timed steps
 (forward 4*B*H*N^2*d, backward 10*B*H*N^2*d, each halved when causal) with
 inputs resident in HBM. ``roofline`` describes the dominant launch, timed with
-HIP events on the stream the kernels run on. ``cpu_baseline`` times the fp64
+HIP events on the stream the kernels run on (on every fourth timed step by
+default: events on every step add 4-6 % to the step time). ``cpu_baseline`` times the fp64
 oracle on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
@@ -121,6 +122,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--warmup-min-s", type=float, default=0.25,
+                   help="after the --warmup steps, keep warming up (whole steps, untimed) "
+                        "until this much wall time has passed (0 disables)")
+    p.add_argument("--event-every", type=int, default=4,
+                   help="record the per-launch HIP events on every n-th timed step only "
+                        "(default 4; 1 = every step, which adds 4-6 %% to the step time)")
     p.add_argument("--no-clock-soak", action="store_true",
                    help="skip the untimed runs after each timed loop that let the SMU's clock "
                         "reading settle (for profiler runs: the trace then holds only the "
@@ -532,22 +539,41 @@ def main():
             if ev is not None:
                 ev[2].record(stream)
 
+    w0 = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The warm-up lasts at least --warmup-min-s of wall time: after idle the
+    # GPU needs on the order of 0.1 s of load to leave its low clock, and a
+    # handful of warm-up steps (a few ms) leave the timed steps on the ramp
+    # (workload 5, 20 timed steps: 0.222 ms per step after 5 warm-up steps,
+    # 0.189 after 500). The extra steps are counted in the line.
+    warm_extra = 0
+    while time.perf_counter() - w0 < args.warmup_min_s:
+        for _ in range(5):
+            step()
+        warm_extra += 5
+        torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Per-launch HIP events on every `event_every`-th timed step: a record
+    # before and after each launch on the launch stream. Events on every step
+    # cost 4-6 % of the workload-5 step time (measured in one process), on
+    # every fourth step about 1 %.
+    every = max(1, args.event_every)
+    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for i in range(0, args.steps, every)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     m0 = time.monotonic()
     for i in range(args.steps):
-        step(events[i])
+        step(events.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     clock.mark("step", m0, time.monotonic())
 
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in events] if w.backward else [0.0] * args.steps
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events.values()]
+    bwd_ms = ([e[1].elapsed_time(e[2]) for e in events.values()] if w.backward
+              else [0.0] * len(events))
 
     # One cold step: a 512 MiB write first evicts the inputs from the L2s and
     # the memory-side cache.
@@ -700,6 +726,8 @@ def main():
                    "causal": w.causal, "key_scale": w.key_scale,
                    "pass": "fwd+bwd" if w.backward else "fwd"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "event_steps": len(events),
+        "warmup_extra_steps": warm_extra,
         "fwd": {"avg_ms": round(f_avg, 4), "median_ms": round(median(fwd_ms), 4),
                 "min_ms": round(min(fwd_ms), 4), "cold_ms": round(cold_fwd_ms, 4),
                 "tflops": round(fwd_tf, 2),
