@@ -15,7 +15,8 @@ The functions ``fa_fwd``, ``fa_fwd_persistent``, ``fa_fwd_kernel_name``, ``fa_bw
 ``fa_decode_workspace_bytes`` and ``fa_strerror`` are the raw C entry points
 (ctypes). ``fwd`` / ``bwd`` / ``unfused_fwd`` / ``fa1_fwd`` / ``decode_fwd`` are
 tensor-level wrappers with the same semantics (``fwd_persistent`` for the
-persistent comparator).
+persistent comparator). ``attention`` wraps ``fwd`` and ``bwd`` as one
+autograd operation.
 """
 from __future__ import annotations
 
@@ -398,3 +399,46 @@ def decode_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out
     if rc != FA_OK:
         raise FAError(rc, "fa_decode_fwd")
     return out, lse
+
+
+# ----------------------------------------------------------------- autograd
+_AttentionFn = None
+
+
+def _attention_fn():
+    """torch.autograd.Function over fa_fwd / fa_bwd, built on first use (so
+    that importing this module does not import torch)."""
+    global _AttentionFn
+    if _AttentionFn is None:
+        import torch
+
+        class AttentionFn(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, causal, scale):
+                o, lse = fwd(q, k, v, causal=causal, scale=scale)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.causal, ctx.scale = causal, scale
+                return o
+
+            @staticmethod
+            def backward(ctx, grad_o):
+                q, k, v, o, lse = ctx.saved_tensors
+                do = grad_o
+                if do.dtype != torch.bfloat16 or not do.is_contiguous():
+                    do = do.to(torch.bfloat16).contiguous()
+                dq, dk, dv = bwd(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale)
+                return dq, dk, dv, None, None
+
+        _AttentionFn = AttentionFn
+    return _AttentionFn
+
+
+def attention(q, k, v, *, causal: bool = False, scale: float | None = None):
+    """O = softmax(scale * Q K^T) V for bf16 [B,H,N,d] GPU tensors, as an
+    autograd operation: the forward pass is ``fwd`` (the per-row logsumexp is
+    kept for the backward), the backward pass is ``bwd`` on the incoming
+    gradient (converted to contiguous bf16 if it is not). Gradients flow to q,
+    k and v."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _attention_fn().apply(q, k, v, bool(causal), float(scale))

@@ -99,3 +99,13 @@ def test_entry_module_has_build_and_smoke():
     if not _gpu_present():
         with pytest.raises(AssertionError, match="needs a GPU"):
             g.smoke()
+
+
+def test_autograd_wrapper_refuses_cpu_tensors():
+    # fa.attention checks its inputs like fwd: CPU tensors never reach the
+    # library (and there is no CPU path to fall back to).
+    torch = pytest.importorskip("torch")
+    from exact_io_aware_12_amd import fa
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, requires_grad=True)
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        fa.attention(q, q, q, causal=True)
