@@ -255,8 +255,15 @@ def long_forwards(fa, torch, fi, dev, clock, soak, warmup=20, calls=50, warmup_m
     return out
 
 
-def cpu_baseline(w, inp, budget_s):
-    """Time the oracle (as it stands) on a bounded sample of heads."""
+# Stated parity bounds (max abs error against the fp64 oracle), per output.
+TOLS = {"O": 2e-2, "LSE": 1e-3, "dQ": 5e-2, "dK": 5e-2, "dV": 5e-2}
+
+
+def cpu_baseline(w, inp, budget_s, gpu_out=None):
+    """Time the oracle (as it stands) on a bounded sample of heads. With the
+    GPU's outputs of the same inputs (`gpu_out`: name -> float64 array of the
+    whole [B,H,...] output), also report their max / mean abs error against
+    the oracle's on the sampled heads (compared after each head's timing)."""
     import numpy as np
     import oracle
     from exact_io_aware_12_amd.inputs import bf16_bits_to_f64
@@ -265,16 +272,23 @@ def cpu_baseline(w, inp, budget_s):
     done, flops, t_total = 0, 0.0, 0.0
     per_head_fwd = w.fwd_flops() / len(heads)
     per_head_bwd = w.bwd_flops() / len(heads) if w.backward else 0.0
+    err = {}
     for b, h in heads:
         q = bf16_bits_to_f64(inp.q[b, h]); k = bf16_bits_to_f64(inp.k[b, h])
         v = bf16_bits_to_f64(inp.v[b, h])
         t0 = time.perf_counter()
-        oracle.attention_fwd(q, k, v, w.scale, w.causal)
+        outs = oracle.attention_fwd(q, k, v, w.scale, w.causal)
         if w.backward:
-            oracle.attention_bwd(q, k, v, bf16_bits_to_f64(inp.do[b, h]), w.scale, w.causal)
+            outs = tuple(outs) + tuple(oracle.attention_bwd(
+                q, k, v, bf16_bits_to_f64(inp.do[b, h]), w.scale, w.causal))
         t_total += time.perf_counter() - t0
         done += 1
         flops += per_head_fwd + per_head_bwd
+        if gpu_out is not None:
+            for name, ref in zip(("O", "LSE", "dQ", "dK", "dV"), outs):
+                e = np.abs(gpu_out[name][b, h] - np.asarray(ref))
+                m, s_, n = err.get(name, (0.0, 0.0, 0))
+                err[name] = (max(m, float(e.max())), s_ + float(e.sum()), n + e.size)
         if t_total >= budget_s:
             break
     rec = {
@@ -290,7 +304,23 @@ def cpu_baseline(w, inp, budget_s):
     }
     if inp.q32 is not None:
         rec["fp32_input_context"] = fp32_input_context(w, inp)
+    if err:
+        rec["parity_vs_oracle"] = {
+            "heads": f"{done} of {len(heads)}",
+            **{name: {"max_abs": m, "mean_abs": s_ / n, "tol": TOLS[name], "pass": m <= TOLS[name]}
+               for name, (m, s_, n) in err.items()}}
     return rec
+
+
+def versions(torch) -> dict:
+    """ROCm (from the install's version file), torch and its HIP runtime."""
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"rocm": rocm, "torch": torch.__version__, "torch_hip": torch.version.hip}
 
 
 def blas_threads() -> int:
@@ -617,6 +647,10 @@ def main():
                 "frac": round(dom["achieved"] / PEAK_BF16_TFLOPS, 4),
                 "traffic": dom["traffic"],
                 "kernel": dom["launch"], "avg_launch_ms": round(dom["avg_ms"], 4)}
+    if dom["traffic"] is not None:
+        # Counter-based HBM rate of the dominant launch (recorded bytes per
+        # launch over this run's average launch time).
+        roofline["traffic_GBs"] = round(dom["traffic"] / (dom["avg_ms"] * 1e-3) / 1e9, 1)
 
     unfused = None
     if args.unfused:
@@ -734,6 +768,10 @@ def main():
                    "causal": w.causal, "key_scale": w.key_scale,
                    "pass": "fwd+bwd" if w.backward else "fwd"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "seed": w.seed,
+        "flops": {"fwd": w.fwd_flops(), "bwd": w.bwd_flops() if w.backward else 0.0},
+        "bytes_alg": {"fwd": fwd_bytes(w), "bwd": bwd_bytes(w) if w.backward else 0},
+        "versions": versions(torch),
         "event_steps": len(events),
         "warmup_extra_steps": warm_extra,
         "fwd": {"avg_ms": round(f_avg, 4), "median_ms": round(median(fwd_ms), 4),
@@ -774,7 +812,15 @@ def main():
         c = clocks.get(ent["workload"])
         ent["sclk_mhz_mean"] = c["mean"] if c else None
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        def f64(t):
+            return t.float().cpu().numpy().astype("float64")
+        gpu_out = {"O": f64(o), "LSE": f64(lse)}
+        if w.backward:
+            gpu_out.update({"dQ": f64(dq), "dK": f64(dk), "dV": f64(dv)})
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, gpu_out)
+        par = rec["cpu_baseline"].pop("parity_vs_oracle", None)
+        if par is not None:
+            rec["parity_vs_oracle"] = par
     print(json.dumps(rec), flush=True)
 
 
