@@ -285,7 +285,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int row = lrow + lane / CPR;
         const int c = (lane % CPR) ^ sw_xor<RB>(row);
         const int src_row = full ? row0 + row : min(row0 + row, N - 1);
-        const uint32_t voff = (uint32_t)(src_row * RB + c * 16);
+        // Unsigned: src_row * RB reaches 2^32 - RB when N * d approaches the
+        // entry points' 2^31 - 1 limit (B = H = 1), past the int range.
+        const uint32_t voff = (uint32_t)src_row * (uint32_t)RB + (uint32_t)(c * 16);
         lds_copy16s(Qh, voff, lds_addr(qbuf(b) + lrow * RB));
         lds_copy16s(dOh, voff, lds_addr(obuf(b) + lrow * RB));
       }
