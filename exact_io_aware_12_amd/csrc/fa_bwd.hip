@@ -667,19 +667,29 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // 8*(t&1) .. +7 of the block: k-slot s of half h is key 8*(s/4) + 4h + s%4
   // of the group, the order of the transposing K reads), dQ^T += K^T dS^T.
   // `copy(c)` is called once after each k-step of the first block: the
-  // next tile's copies, spread over the MFMA stream.
+  // next tile's copies, spread over the MFMA stream. The second block's
+  // S^T / dP^T MFMAs come before the first block's dQ^T MFMAs, so that the
+  // first block's exp / dS work and the second block's MFMAs (independent of
+  // each other) sit together for the scheduler to interleave; every dQ^T
+  // accumulator still takes its four MFMAs in the same order (-0.5 to -1.7 %
+  // on the backward, bit-identical).
   auto tile = [&](const uint8_t* kt, const uint8_t* vt, int kbase, bool masked, auto&& copy)
                   __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      f32x16 sa = zero16(), pa = zero16();
+    // S^T and dP^T of 32-key block kb.
+    auto sdp = [&](int kb, f32x16& sa, f32x16& pa, bool with_copy) __attribute__((always_inline)) {
+      sa = zero16();
+      pa = zero16();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int o = kb * 32 * RB + rk_off[ks];
         sa = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(kt + o), qreg[ks], sa);
         pa = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(vt + o), doreg[ks], pa);
-        if (kb == 0) copy(ks);
+        if (with_copy) copy(ks);
       }
+    };
+    // Exponent, mask, P^T, dS^T of block kb, packed per 16-key group.
+    auto ds_block = [&](int kb, f32x16& sa, const f32x16& pa, bf16x8 (&sb)[2])
+                        __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sa[i] = fmaf(sa[i], c2, nlse2);
       if (masked) {
@@ -691,17 +701,32 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
-        const int t = 2 * kb + th;
         float ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ds[e] = fast_exp2(sa[8 * th + e]) * (pa[8 * th + e] - drow);
-        const bf16x8 sb = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        sb[th] = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      }
+    };
+    // dQ^T += K^T dS^T for block kb's two 16-key groups.
+    auto dq_block = [&](int kb, const bf16x8 (&sb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        const int t = 2 * kb + th;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           dqacc[db] = mfma_32x32x16(tr_operand(kt + 16 * t * RB, tk_off[0][db], tk_off[1][db]),
-                                    sb, dqacc[db]);
+                                    sb[th], dqacc[db]);
       }
-    }
+    };
+    static_assert(NB == 2, "two 32-key blocks per key tile");
+    f32x16 sa, pa;
+    bf16x8 sb0[2], sb1[2];
+    sdp(0, sa, pa, true);
+    ds_block(0, sa, pa, sb0);
+    sdp(1, sa, pa, false);
+    dq_block(0, sb0);
+    ds_block(1, sa, pa, sb1);
+    dq_block(1, sb1);
   };
 
   wait_vmem();
