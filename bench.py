@@ -523,8 +523,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(attention shards by head with no exchange; see the design notes). "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(attention shards by head with no exchange, so each GPU would run the "
+              "same kernels on its share of the heads). "
               f"Asked for --gpus {args.gpus} (WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
