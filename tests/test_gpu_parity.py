@@ -485,3 +485,36 @@ def test_random_shapes_fwd_bwd(fa, B, H, N, d, causal, scale):
     # The stated absolute gradient bound is for 1/sqrt(d); other scales use
     # the relative form (parity_util.assert_close_rel).
     _check_bwd(fa, B, H, N, d, causal, seed=seed + 10, scale=scale, relative=scale is not None)
+
+
+# ---------------------------------------------------------------- long backward
+# The backward at long sequences (hundreds of query / key tiles per head, the
+# causal pairing of key tiles far apart, the dQ kernel without the key split),
+# every element of the sampled heads against the oracle's full backward.
+@pytest.mark.parametrize("B,H,N,d,causal,heads", [
+    (1, 16, 16384, 128, True, [0, 15]),
+    (1, 8, 8192, 64, False, [3]),
+    (1, 4, 12289, 128, True, [2]),
+])
+def test_bwd_long_sequences(fa, B, H, N, d, causal, heads):
+    import torch
+    print(f"[bwd long] B={B} H={H} N={N} d={d} causal={causal} heads={heads} "
+          f"kernels={fa.fa_bwd_kernel_name(B, H, N, d, causal)}", flush=True)
+    shape = (B, H, N, d)
+    seed = 12000 + N + d
+    qb, kb, vb, dob = (fi.random_bf16(shape, seed + i) for i in range(4))
+    scale = 1 / math.sqrt(d)
+    o, lse, (q, k, v) = _run_fwd(fa, qb, kb, vb, scale, causal)
+    dq, dk, dv = fa.bwd(q, k, v, o, to_gpu_bf16(dob), lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    got = [from_gpu(t) for t in (dq, dk, dv)]
+    sel = [(0, h) for h in heads]
+
+    def ref(bh):
+        b, h = bh
+        return oracle.attention_bwd(bits_to_f64(qb[b, h]), bits_to_f64(kb[b, h]),
+                                    bits_to_f64(vb[b, h]), bits_to_f64(dob[b, h]), scale, causal)
+
+    for (b, h), r in zip(sel, map_heads(ref, sel)):
+        for name, g, rr in zip(("dQ", "dK", "dV"), got, r):
+            assert_close(f"{name}[{b},{h}]", g[b, h], rr, TOL_GRAD)
