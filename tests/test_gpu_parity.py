@@ -263,6 +263,50 @@ def test_bwd_deterministic(fa):
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))
 
 
+def test_concurrent_streams_and_threads(fa):
+    """Four host threads, each on its own stream, run fwd + bwd on their own
+    inputs at the same time (the library keeps no state between calls); every
+    result equals the same call made alone."""
+    import threading
+    import torch
+    shapes = [(1, 4, 700, 128, True), (2, 2, 513, 64, False), (1, 3, 1000, 128, False),
+              (1, 2, 300, 64, True)]
+    inputs = [[to_gpu_bf16(fi.random_bf16(sh[:4], 4500 + 10 * i + j)) for j in range(4)]
+              for i, sh in enumerate(shapes)]
+
+    def run(i):
+        q, k, v, do = inputs[i]
+        causal = shapes[i][4]
+        o, lse = fa.fwd(q, k, v, causal=causal)
+        return (o, lse) + tuple(fa.bwd(q, k, v, o, do, lse, causal=causal))
+
+    alone = [run(i) for i in range(len(shapes))]
+    torch.cuda.synchronize()
+    results = [None] * len(shapes)
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    results[i] = run(i)
+            s.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(shapes)):
+        for a, b in zip(results[i], alone[i]):
+            assert torch.equal(a, b), f"case {i}: concurrent result differs"
+
+
 def test_bwd_scale_zero_and_negative(fa):
     _check_bwd(fa, 1, 2, 200, 128, True, seed=3, scale=0.0)
     _check_bwd(fa, 1, 2, 200, 64, False, seed=4, scale=-0.3)
