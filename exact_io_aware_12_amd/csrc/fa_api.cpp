@@ -19,6 +19,7 @@ hipError_t fwd_persistent_dispatch(const uint16_t* q, const uint16_t* k, const u
 bool fwd_uses_two_group_kernel(int BH, int N, int d, bool causal);
 bool fwd_uses_split_kernel(int BH, int N, int d);
 bool fwd_uses_split_groups(int BH, int N, int d);
+bool fwd_uses_paired_split(int BH, int N, int d, bool causal);
 bool bwd_dq_uses_split(int BH, int N, bool causal);
 hipError_t bwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* o, const uint16_t* dout, const float* lse,
@@ -75,6 +76,8 @@ int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, floa
 
 const char* fa_fwd_kernel_name(int B, int H, int N, int d, int causal) {
   if (check_shape(B, H, N, d) != FA_OK) return nullptr;
+  if (fa::fwd_uses_paired_split(B * H, N, d, causal != 0))
+    return "fa_fwd_pp_kernel (keys split between the groups, two query tiles per workgroup)";
   if (fa::fwd_uses_split_kernel(B * H, N, d)) return "fa_fwd_pp_kernel (keys split between the groups)";
   if (fa::fwd_uses_split_groups(B * H, N, d)) return "fa_fwd_kernel (keys split between two groups)";
   return fa::fwd_uses_two_group_kernel(B * H, N, d, causal != 0) ? "fa_fwd_pp_kernel"

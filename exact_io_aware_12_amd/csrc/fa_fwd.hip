@@ -719,6 +719,11 @@ static hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_
 // and stores. On such grids the one-group kernel leaves one wave per SIMD
 // with nothing to overlap with; here two waves of each SIMD alternate MFMA
 // and VALU clusters, and the longest row's key tiles are shared by two waves.
+//
+// PAIR (causal SPLIT grids of up to two 128-row tiles per CU): each
+// workgroup runs two query tiles one after the other, the heavy tile
+// ntq-1-u and the light tile u, so all workgroups have the same number of
+// key tiles and the grid fits in one round.
 // ---------------------------------------------------------------------------
 struct PingPongCfg {
   static constexpr int D = 128, BM = 256, THREADS = 512, BN = 64, RB = 256;
@@ -728,7 +733,7 @@ struct PingPongCfg {
 };
 
 
-template <bool CAUSAL, bool POS, bool SPLIT>
+template <bool CAUSAL, bool POS, bool SPLIT, bool PAIR = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_pp_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
@@ -766,283 +771,299 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       rank = b / BH;
     }
   }
-  const int qt = CAUSAL ? (ntq - 1 - rank) : rank;
-  const int q0 = qt * BMQ;
-  const int qw = q0 + 32 * blk;
-  const int qrow = qw + l32;
-  const size_t off = (size_t)head * N * D;
-  const uint16_t* Kh = K + off;
-  const uint16_t* Vh = V + off;
+  static_assert(!PAIR || (SPLIT && CAUSAL), "pairs are causal split-key tiles");
+  // One query tile `qt` (128 rows with SPLIT, else 256).
+  auto item = [&](const int qt) __attribute__((always_inline)) {
+    const int q0 = qt * BMQ;
+    const int qw = q0 + 32 * blk;
+    const int qrow = qw + l32;
+    const size_t off = (size_t)head * N * D;
+    const uint16_t* Kh = K + off;
+    const uint16_t* Vh = V + off;
 
-  const int kend = CAUSAL ? min(N, q0 + BMQ) : N;
-  const int nt = (kend + BN - 1) / BN;
-  const int ntw_all = CAUSAL ? min(nt, (min(N, qw + 32) + BN - 1) / BN) : nt;
-  // Steps (the same for every wave) and this wave's computed local tiles.
-  const int ns = SPLIT ? (nt + 1) >> 1 : nt;
-  const int ntw = SPLIT ? (ntw_all - grp + 1) >> 1 : ntw_all;
-  auto key_tile = [&](int j) { return SPLIT ? 2 * j + grp : j; };
+    const int kend = CAUSAL ? min(N, q0 + BMQ) : N;
+    const int nt = (kend + BN - 1) / BN;
+    const int ntw_all = CAUSAL ? min(nt, (min(N, qw + 32) + BN - 1) / BN) : nt;
+    // Steps (the same for every wave) and this wave's computed local tiles.
+    const int ns = SPLIT ? (nt + 1) >> 1 : nt;
+    const int ntw = SPLIT ? (ntw_all - grp + 1) >> 1 : ntw_all;
+    auto key_tile = [&](int j) { return SPLIT ? 2 * j + grp : j; };
 
-  static_assert(FC::LOADS == C::LOADS, "copy layout shared with fa_fwd_kernel");
-  // This group's 4 waves copy tile t (tiles past the last repeat it: in
-  // bounds, unused) of K (IS_V false) or V into dst, in the layout of
-  // fa_fwd_kernel's copies (rows past N read row N-1). The per-lane offsets
-  // are formed here, in the VALU cluster, rather than held in registers.
-  auto copy_tile = [&](auto is_v, uint8_t* dst, int t) __attribute__((always_inline)) {
-    constexpr bool IS_V = decltype(is_v)::value;
-    const int kb0 = min(key_tile(t), nt - 1) * BN;
-    const int rmax = N - 1 - kb0;
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int r = dma_row<128, IS_V>(w, i, lane);
-      const uint32_t o = (uint32_t)(min(r, rmax) * D + dma_col<128, IS_V>(r, lane)) * 2u;
-      lds_copy16((IS_V ? Vh : Kh) + (size_t)kb0 * D, o,
-                 lds_addr_of(dst + gofs + (w * C::LOADS + i) * 1024));
+    static_assert(FC::LOADS == C::LOADS, "copy layout shared with fa_fwd_kernel");
+    // This group's 4 waves copy tile t (tiles past the last repeat it: in
+    // bounds, unused) of K (IS_V false) or V into dst, in the layout of
+    // fa_fwd_kernel's copies (rows past N read row N-1). The per-lane offsets
+    // are formed here, in the VALU cluster, rather than held in registers.
+    auto copy_tile = [&](auto is_v, uint8_t* dst, int t) __attribute__((always_inline)) {
+      constexpr bool IS_V = decltype(is_v)::value;
+      const int kb0 = min(key_tile(t), nt - 1) * BN;
+      const int rmax = N - 1 - kb0;
+  #pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int r = dma_row<128, IS_V>(w, i, lane);
+        const uint32_t o = (uint32_t)(min(r, rmax) * D + dma_col<128, IS_V>(r, lane)) * 2u;
+        lds_copy16((IS_V ? Vh : Kh) + (size_t)kb0 * D, o,
+                   lds_addr_of(dst + gofs + (w * C::LOADS + i) * 1024));
+      }
+    };
+    using KT = std::integral_constant<bool, false>;
+    using VT = std::integral_constant<bool, true>;
+
+    bf16x8 qreg[C::KS];
+    {
+      const uint16_t* qp = Q + off + (size_t)min(qrow, N - 1) * D + hi * 8;
+  #pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        qreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(qp + ks * 16));
     }
-  };
-  using KT = std::integral_constant<bool, false>;
-  using VT = std::integral_constant<bool, true>;
+    // Prologue copies: K_0 and K_1 (group 0), V_0 and V_1 (group 1); with
+    // SPLIT every group copies its own four.
+    if (SPLIT) {
+      copy_tile(KT{}, kl0, 0);
+      copy_tile(KT{}, kl1, 1);
+      copy_tile(VT{}, vl0, 0);
+      copy_tile(VT{}, vl1, 1);
+    } else if (grp == 0) {
+      copy_tile(KT{}, kl0, 0);
+      copy_tile(KT{}, kl1, 1);
+    } else {
+      copy_tile(VT{}, vl0, 0);
+      copy_tile(VT{}, vl1, 1);
+    }
 
-  bf16x8 qreg[C::KS];
-  {
-    const uint16_t* qp = Q + off + (size_t)min(qrow, N - 1) * D + hi * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      qreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(qp + ks * 16));
-  }
-  // Prologue copies: K_0 and K_1 (group 0), V_0 and V_1 (group 1); with
-  // SPLIT every group copies its own four.
-  if (SPLIT) {
-    copy_tile(KT{}, kl0, 0);
-    copy_tile(KT{}, kl1, 1);
-    copy_tile(VT{}, vl0, 0);
-    copy_tile(VT{}, vl1, 1);
-  } else if (grp == 0) {
-    copy_tile(KT{}, kl0, 0);
-    copy_tile(KT{}, kl1, 1);
-  } else {
-    copy_tile(VT{}, vl0, 0);
-    copy_tile(VT{}, vl1, 1);
-  }
+    int koff[C::KS];
+  #pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) koff[ks] = k_off<D>(l32, 2 * ks + hi) + gofs;
+    int voff[C::DB];
+    {
+      const int g = lane >> 4, sl = lane & 15;
+  #pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        voff[db] = v_off<D>(4 * hi + (sl >> 2), 32 * db + 16 * (g & 1) + 4 * (sl & 3)) + gofs;
+    }
 
-  int koff[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = k_off<D>(l32, 2 * ks + hi) + gofs;
-  int voff[C::DB];
-  {
-    const int g = lane >> 4, sl = lane & 15;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-      voff[db] = v_off<D>(4 * hi + (sl >> 2), 32 * db + 16 * (g & 1) + 4 * (sl & 3)) + gofs;
-  }
+    f32x16 oacc[C::DB];
+  #pragma unroll
+    for (int i = 0; i < C::DB; ++i) oacc[i] = zero16();
+    f32x16 sacc[C::NB];
+    bf16x8 pk[BN / 16];
+    float m_run = -INFINITY, l_run = 0.f;
 
-  f32x16 oacc[C::DB];
-#pragma unroll
-  for (int i = 0; i < C::DB; ++i) oacc[i] = zero16();
-  f32x16 sacc[C::NB];
-  bf16x8 pk[BN / 16];
-  float m_run = -INFINITY, l_run = 0.f;
-
-  auto scores = [&](const uint8_t* kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < C::NB; ++kb) sacc[kb] = zero16();
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < C::NB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * RB + koff[ks]);
-        sacc[kb] = mfma_32x32x16(a, qreg[ks], sacc[kb]);
-      }
-  };
-  auto pv = [&](const uint8_t* vt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < BN / 16; ++t)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const uint8_t* vp = vt + 16 * t * RB + voff[db];
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)vp);
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp + 8 * RB));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = mfma_32x32x16(a, pk[t], oacc[db]);
-      }
-  };
-  // Statistics of tile kbase (as in fa_fwd_kernel), then P = exp2(s - m) for
-  // it, its row sum and bf16 packing into the next PV operands.
-  auto softmax = [&](int kbase) __attribute__((always_inline)) {
-    const bool masked = (CAUSAL && kbase + BN - 1 > qw) || (kbase + BN > N);
-    if (masked) {
-#pragma unroll
-      for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          const bool ok = key < N && (!CAUSAL || key <= qrow);
-          if constexpr (POS) sacc[kb][i] = ok ? sacc[kb][i] : -INFINITY;
-          else sacc[kb][i] = ok ? sacc[kb][i] * c2 : -INFINITY;
+    auto scores = [&](const uint8_t* kt) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int kb = 0; kb < C::NB; ++kb) sacc[kb] = zero16();
+  #pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+  #pragma unroll
+        for (int kb = 0; kb < C::NB; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * RB + koff[ks]);
+          sacc[kb] = mfma_32x32x16(a, qreg[ks], sacc[kb]);
         }
-    } else if constexpr (!POS) {
-#pragma unroll
+    };
+    auto pv = [&](const uint8_t* vt) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int t = 0; t < BN / 16; ++t)
+  #pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const uint8_t* vp = vt + 16 * t * RB + voff[db];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)vp);
+          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vp + 8 * RB));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = mfma_32x32x16(a, pk[t], oacc[db]);
+        }
+    };
+    // Statistics of tile kbase (as in fa_fwd_kernel), then P = exp2(s - m) for
+    // it, its row sum and bf16 packing into the next PV operands.
+    auto softmax = [&](int kbase) __attribute__((always_inline)) {
+      const bool masked = (CAUSAL && kbase + BN - 1 > qw) || (kbase + BN > N);
+      if (masked) {
+  #pragma unroll
+        for (int kb = 0; kb < C::NB; ++kb)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const bool ok = key < N && (!CAUSAL || key <= qrow);
+            if constexpr (POS) sacc[kb][i] = ok ? sacc[kb][i] : -INFINITY;
+            else sacc[kb][i] = ok ? sacc[kb][i] * c2 : -INFINITY;
+          }
+      } else if constexpr (!POS) {
+  #pragma unroll
+        for (int kb = 0; kb < C::NB; ++kb)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[kb][i] *= c2;
+      }
+      float tmax = tile_max<C::NB>(sacc);
+      if constexpr (POS) tmax *= c2;
+      tmax = halves_max(tmax);
+      const bool grow = tmax > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? tmax : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+        m_run = m_new;
+        l_run *= alpha;
+  #pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+  #pragma unroll
       for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] *= c2;
-    }
-    float tmax = tile_max<C::NB>(sacc);
-    if constexpr (POS) tmax *= c2;
-    tmax = halves_max(tmax);
-    const bool grow = tmax > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? tmax : m_run;
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-    for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if constexpr (POS) sacc[kb][i] = fast_exp2(fmaf(sacc[kb][i], c2, -m_use));
-        else sacc[kb][i] = fast_exp2(sacc[kb][i] - m_use);
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if constexpr (POS) sacc[kb][i] = fast_exp2(fmaf(sacc[kb][i], c2, -m_use));
+          else sacc[kb][i] = fast_exp2(sacc[kb][i] - m_use);
+        }
+      l_run += tile_sum<C::NB>(sacc);
+  #pragma unroll
+      for (int t = 0; t < BN / 16; ++t) {
+        const f32x16& p = sacc[t >> 1];
+        const int r0 = (t & 1) * 8;
+        pk[t] = pack_bf16x8(p[r0 + 0], p[r0 + 1], p[r0 + 2], p[r0 + 3],
+                            p[r0 + 4], p[r0 + 5], p[r0 + 6], p[r0 + 7]);
       }
-    l_run += tile_sum<C::NB>(sacc);
-#pragma unroll
-    for (int t = 0; t < BN / 16; ++t) {
-      const f32x16& p = sacc[t >> 1];
-      const int r0 = (t & 1) * 8;
-      pk[t] = pack_bf16x8(p[r0 + 0], p[r0 + 1], p[r0 + 2], p[r0 + 3],
-                          p[r0 + 4], p[r0 + 5], p[r0 + 6], p[r0 + 7]);
-    }
-  };
+    };
 
-  // MFMA cluster of tile j: scores of tile j+1 from k_next (computed on the
-  // wave's last tile too, from whatever the buffer holds, never used: one
-  // code path) and O += V_j P_j; then the wait for this wave's copies of the
-  // previous VALU cluster (only group 1 copies).
-  auto mcluster = [&](int j, const uint8_t* k_next, const uint8_t* v_this) __attribute__((always_inline)) {
-    if (j < ntw) {
-      scores(k_next);
-      pv(v_this);
-      constexpr int kMfma = 0x008, kDsRead = 0x100;
-      // Operand reads run a few MFMAs ahead: one K read per score MFMA,
-      // then two transposing V reads per PV MFMA.
-      __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * C::KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    // MFMA cluster of tile j: scores of tile j+1 from k_next (computed on the
+    // wave's last tile too, from whatever the buffer holds, never used: one
+    // code path) and O += V_j P_j; then the wait for this wave's copies of the
+    // previous VALU cluster (only group 1 copies).
+    auto mcluster = [&](int j, const uint8_t* k_next, const uint8_t* v_this) __attribute__((always_inline)) {
+      if (j < ntw) {
+        scores(k_next);
+        pv(v_this);
+        constexpr int kMfma = 0x008, kDsRead = 0x100;
+        // Operand reads run a few MFMAs ahead: one K read per score MFMA,
+        // then two transposing V reads per PV MFMA.
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 4, 0);
+  #pragma unroll
+        for (int i = 0; i < 2 * C::KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        }
+  #pragma unroll
+        for (int i = 0; i < 4 * C::DB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 4 * C::DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
-      }
-    }
-    wait_dma();
-  };
+      wait_dma();
+    };
 
-  wait_dma();
-  __syncthreads();
-  // Prologue: every wave forms P_0 from K_0.
-  if (!SPLIT || ntw > 0) {
-    scores(kl0);
-    softmax(key_tile(0) * BN);
-  }
-  __syncthreads();
-  // Group 1 starts one cluster later: its first slot copies K_2 into K_0's
-  // buffer (free now) and waits for it; group 0 meanwhile runs M(0). With
-  // SPLIT group 0 copies its own K_2 there too, waited for at the end of M(0).
-  if (grp == 1) {
-    copy_tile(KT{}, kl0, 2);
     wait_dma();
     __syncthreads();
-  } else if (SPLIT) {
-    copy_tile(KT{}, kl0, 2);
-  }
-
-  // Every wave runs the same clusters: M(j), barrier, V(j), barrier. With
-  // group 1 one barrier behind, one wave of each SIMD is in an MFMA cluster
-  // while the other is in a VALU cluster. V(j) is the softmax of tile j+1
-  // and, for group 1, the copies of K_{j+3} (into K_{j+1}'s buffer) and
-  // V_{j+2} (into V_j's), both last read by M(j) of the two groups.
-  auto step = [&](auto ph, int j) __attribute__((always_inline)) {
-    constexpr int P = decltype(ph)::value;   // j % 2
-    const uint8_t* const k_next = P ? kl0 : kl1;   // K_{j+1}
-    const uint8_t* const v_this = P ? vl1 : vl0;   // V_j
-    uint8_t* const k_fill = P ? kl0 : kl1;         // K_{j+1}'s buffer, gets K_{j+3}
-    uint8_t* const v_fill = P ? vl1 : vl0;         // V_j's buffer, gets V_{j+2}
-    mcluster(j, k_next, v_this);
-    __syncthreads();
-    if (j + 1 < ntw) softmax(key_tile(j + 1) * BN);
-    if (SPLIT || grp == 1) {
-      copy_tile(KT{}, k_fill, j + 3);
-      copy_tile(VT{}, v_fill, j + 2);
+    // Prologue: every wave forms P_0 from K_0.
+    if (!SPLIT || ntw > 0) {
+      scores(kl0);
+      softmax(key_tile(0) * BN);
     }
     __syncthreads();
-  };
-  for (int j = 0; j < ns; j += 2) {
-    step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < ns) step(std::integral_constant<int, 1>{}, j + 1);
-  }
-  if (grp == 0) __syncthreads();
-  wait_dma();
-  // Every wave's copies have landed and every read is done: the four tile
-  // buffers hold the 8 waves' O rows on their way out (8 KiB per wave).
-  __syncthreads();
-
-  if constexpr (SPLIT) {
-    // Group 1 hands its reference max, its row-half sums and its O^T partials
-    // to the group-0 wave with the same rows and lanes (through its own LDS
-    // halves), which rescales both to the larger max and adds them.
-    float* const xo = reinterpret_cast<float*>((w == 0 ? kl0 : w == 1 ? kl1 : w == 2 ? vl0 : vl1) + C::TILE);
-    float* const xs = reinterpret_cast<float*>(vl1) + w * 128;
+    // Group 1 starts one cluster later: its first slot copies K_2 into K_0's
+    // buffer (free now) and waits for it; group 0 meanwhile runs M(0). With
+    // SPLIT group 0 copies its own K_2 there too, waited for at the end of M(0).
     if (grp == 1) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(xo + ((db * 4 + q4) * 64 + lane) * 4) =
-              f32x4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
-      xs[lane] = m_run;
-      xs[64 + lane] = l_run;
+      copy_tile(KT{}, kl0, 2);
+      wait_dma();
+      __syncthreads();
+    } else if (SPLIT) {
+      copy_tile(KT{}, kl0, 2);
     }
-    __syncthreads();
-    if (grp == 1) return;
-    const float m1 = xs[lane], l1 = xs[64 + lane];
-    const float m = vmax(m_run, m1);
-    const float mu = m == -INFINITY ? 0.f : m;
-    const float a0 = fast_exp2(m_run - mu), a1 = fast_exp2(m1 - mu);
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 p = *reinterpret_cast<const f32x4*>(xo + ((db * 4 + q4) * 64 + lane) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[db][4 * q4 + e] = fmaf(p[e], a1, oacc[db][4 * q4 + e] * a0);
-      }
-    l_run = fmaf(l1, a1, l_run * a0);
-    m_run = m;
-  }
 
-  const float l_tot = halves_sum(l_run);
-  {
-    const float inv = 1.f / l_tot;
-    u32x2 ov[C::DB][4];
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        ov[db][g4] = u32x2{pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
-                           pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-    uint8_t* const buf = blk < 2 ? kl0 : blk < 4 ? kl1 : blk < 6 ? vl0 : vl1;
-    store_rows_staged<D>(O + off + (size_t)qw * D, N - qw, buf + (blk & 1) * 32 * RB, ov, lane);
+    // Every wave runs the same clusters: M(j), barrier, V(j), barrier. With
+    // group 1 one barrier behind, one wave of each SIMD is in an MFMA cluster
+    // while the other is in a VALU cluster. V(j) is the softmax of tile j+1
+    // and, for group 1, the copies of K_{j+3} (into K_{j+1}'s buffer) and
+    // V_{j+2} (into V_j's), both last read by M(j) of the two groups.
+    auto step = [&](auto ph, int j) __attribute__((always_inline)) {
+      constexpr int P = decltype(ph)::value;   // j % 2
+      const uint8_t* const k_next = P ? kl0 : kl1;   // K_{j+1}
+      const uint8_t* const v_this = P ? vl1 : vl0;   // V_j
+      uint8_t* const k_fill = P ? kl0 : kl1;         // K_{j+1}'s buffer, gets K_{j+3}
+      uint8_t* const v_fill = P ? vl1 : vl0;         // V_j's buffer, gets V_{j+2}
+      mcluster(j, k_next, v_this);
+      __syncthreads();
+      if (j + 1 < ntw) softmax(key_tile(j + 1) * BN);
+      if (SPLIT || grp == 1) {
+        copy_tile(KT{}, k_fill, j + 3);
+        copy_tile(VT{}, v_fill, j + 2);
+      }
+      __syncthreads();
+    };
+    for (int j = 0; j < ns; j += 2) {
+      step(std::integral_constant<int, 0>{}, j);
+      if (j + 1 < ns) step(std::integral_constant<int, 1>{}, j + 1);
+    }
+    if (grp == 0) __syncthreads();
+    wait_dma();
+    // Every wave's copies have landed and every read is done: the four tile
+    // buffers hold the 8 waves' O rows on their way out (8 KiB per wave).
+    __syncthreads();
+
+    if constexpr (SPLIT) {
+      // Group 1 hands its reference max, its row-half sums and its O^T partials
+      // to the group-0 wave with the same rows and lanes (through its own LDS
+      // halves), which rescales both to the larger max and adds them.
+      float* const xo = reinterpret_cast<float*>((w == 0 ? kl0 : w == 1 ? kl1 : w == 2 ? vl0 : vl1) + C::TILE);
+      float* const xs = reinterpret_cast<float*>(vl1) + w * 128;
+      if (grp == 1) {
+  #pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+  #pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4*>(xo + ((db * 4 + q4) * 64 + lane) * 4) =
+                f32x4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
+        xs[lane] = m_run;
+        xs[64 + lane] = l_run;
+      }
+      __syncthreads();
+      if (grp == 1) return;
+      const float m1 = xs[lane], l1 = xs[64 + lane];
+      const float m = vmax(m_run, m1);
+      const float mu = m == -INFINITY ? 0.f : m;
+      const float a0 = fast_exp2(m_run - mu), a1 = fast_exp2(m1 - mu);
+  #pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+  #pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 p = *reinterpret_cast<const f32x4*>(xo + ((db * 4 + q4) * 64 + lane) * 4);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[db][4 * q4 + e] = fmaf(p[e], a1, oacc[db][4 * q4 + e] * a0);
+        }
+      l_run = fmaf(l1, a1, l_run * a0);
+      m_run = m;
+    }
+
+    const float l_tot = halves_sum(l_run);
+    {
+      const float inv = 1.f / l_tot;
+      u32x2 ov[C::DB][4];
+  #pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+  #pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          ov[db][g4] = u32x2{pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv),
+                             pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+      uint8_t* const buf = blk < 2 ? kl0 : blk < 4 ? kl1 : blk < 6 ? vl0 : vl1;
+      store_rows_staged<D>(O + off + (size_t)qw * D, N - qw, buf + (blk & 1) * 32 * RB, ov, lane);
+    }
+    if (qrow < N && hi == 0) LSE[(size_t)head * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+  };
+  if constexpr (PAIR) {
+    // Two causal query tiles, the heavy ntq-1-u and then the light u: every
+    // pair has the same number of key tiles (the middle tile of an odd count
+    // is alone).
+    const int qa = ntq - 1 - rank, qb = rank;
+    item(qa);
+    if (qb != qa) {
+      __syncthreads();
+      item(qb);
+    }
+  } else {
+    item(CAUSAL ? (ntq - 1 - rank) : rank);
   }
-  if (qrow < N && hi == 0) LSE[(size_t)head * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
-template <bool CAUSAL, bool POS, bool SPLIT = false>
+template <bool CAUSAL, bool POS, bool SPLIT = false, bool PAIR = false>
 static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 uint16_t* o, float* lse, int BH, int N, float scale,
                                 hipStream_t stream) {
@@ -1050,8 +1071,9 @@ static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint
   const int ntq = (N + bmq - 1) / bmq;
   const int xcd_group = (BH % 8 == 0) ? BH / 8 : 0;
   const float c2 = scale * kLog2e;
-  dim3 grid((unsigned)(ntq * BH)), block(PingPongCfg::THREADS);
-  hipLaunchKernelGGL((fa_fwd_pp_kernel<CAUSAL, POS, SPLIT>), grid, block, 0, stream,
+  const int units = PAIR ? (ntq + 1) / 2 : ntq;   // workgroups per head
+  dim3 grid((unsigned)(units * BH)), block(PingPongCfg::THREADS);
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<CAUSAL, POS, SPLIT, PAIR>), grid, block, 0, stream,
                      q, k, v, o, lse, BH, N, ntq, c2, xcd_group);
   return hipGetLastError();
 }
@@ -1076,10 +1098,29 @@ bool fwd_uses_two_group_kernel(int BH, int N, int d, bool causal) {
          N >= (causal ? 8192 : 4096);
 }
 
+// Causal d = 128 grids of 257-512 128-row query tiles with at least 4096
+// keys take the split-key two-group kernel with two query tiles per
+// workgroup (heavy, then light): one round of at most 256 workgroups, each
+// with the same number of key tiles. Measured against the kernel they took
+// before (fa_fwd_kernel below N = 8192, fa_fwd_pp_kernel from it): -5 to
+// -8 % at N = 4096 (B*H = 12, 16), -18 to -26 % at N = 8192 (B*H = 6, 8),
+// -20 to -30 % at N = 16384 (B*H = 3, 4); but +5 % at N = 2048 (B*H = 32,
+// the fwd+bwd workload's shape) and +24 % at N = 1024, where each tile's
+// start-up and merge weigh more, and +7 to +24 % on grids of more than 512
+// tiles (two rounds).
+bool fwd_uses_paired_split(int BH, int N, int d, bool causal) {
+  const long tiles = (long)((N + 127) / 128) * BH;
+  return d == 128 && causal && N >= 4096 && tiles > 256 && tiles <= 512;
+}
+
 hipError_t fwd_dispatch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* o, float* lse, int BH, int N, int d, float scale,
                         bool causal, hipStream_t stream) {
   const bool pos = scale > 0.f;
+  if (fwd_uses_paired_split(BH, N, d, causal)) {
+    if (pos) return launch_fwd_pp<true, true, true, true>(q, k, v, o, lse, BH, N, scale, stream);
+    return launch_fwd_pp<true, false, true, true>(q, k, v, o, lse, BH, N, scale, stream);
+  }
   if (fwd_uses_split_kernel(BH, N, d)) {
     if (causal && pos) return launch_fwd_pp<true, true, true>(q, k, v, o, lse, BH, N, scale, stream);
     if (!causal && pos) return launch_fwd_pp<false, true, true>(q, k, v, o, lse, BH, N, scale, stream);

@@ -87,6 +87,9 @@ FA355_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float
  *   "fa_fwd_pp_kernel (keys split between the groups)": d = 128, N >= 1024
  *     and at most 256 query tiles of 128 rows; both groups own the same 128
  *     rows, take alternate key tiles and merge their partial results;
+ *   "fa_fwd_pp_kernel (keys split between the groups, two query tiles per
+ *     workgroup)": causal, d = 128, N >= 4096 and 257-512 query tiles of 128
+ *     rows; the same split, each workgroup taking a heavy and a light tile;
  *   "fa_fwd_kernel (keys split between two groups)": d = 64 with the same
  *     grid limits; 8-wave workgroups of two 4-wave groups on the same rows.
  * All compute the same values up to the order of fp32 sums. NULL when the

@@ -39,6 +39,7 @@ hipError_t fwd_persistent_dispatch(const uint16_t*, const uint16_t*, const uint1
 bool fwd_uses_two_group_kernel(int, int N, int d, bool) { return d == 128 && N >= 8192; }
 bool fwd_uses_split_kernel(int, int, int) { return false; }
 bool fwd_uses_split_groups(int, int, int) { return false; }
+bool fwd_uses_paired_split(int, int, int, bool) { return false; }
 bool bwd_dq_uses_split(int BH, int N, bool) { return (int64_t)BH * ((N + 127) / 128) <= 256; }
 
 hipError_t bwd_dispatch(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,

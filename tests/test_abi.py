@@ -43,7 +43,8 @@ def test_header_declares_the_entry_points():
 
 def test_fwd_kernel_name_follows_the_dispatch_rule(fa):
     # Two-group kernel: d = 128, causal N >= 8192 or non-causal N >= 4096, and
-    # at least 256 of its 256-row workgroups; otherwise the 128-row kernel.
+    # at least 256 of its 256-row workgroups (unless a split form applies);
+    # otherwise the 128-row kernel.
     assert fa.fa_fwd_kernel_name(1, 16, 16384, 128, True) == "fa_fwd_pp_kernel"
     assert fa.fa_fwd_kernel_name(2, 32, 4096, 128, True) == "fa_fwd_kernel"
     assert fa.fa_fwd_kernel_name(2, 32, 4096, 128, False) == "fa_fwd_pp_kernel"
@@ -52,7 +53,15 @@ def test_fwd_kernel_name_follows_the_dispatch_rule(fa):
     assert fa.fa_fwd_kernel_name(1, 1, 16384, 128, True) == split     # 128 tiles of 128 rows
     assert fa.fa_fwd_kernel_name(1, 2, 16384, 128, False) == split    # 256: one per CU
     assert fa.fa_fwd_kernel_name(1, 3, 1500, 128, True) == split
-    assert fa.fa_fwd_kernel_name(1, 3, 16384, 128, True) == "fa_fwd_kernel"   # 384 tiles, 192 of 256 rows
+    paired = "fa_fwd_pp_kernel (keys split between the groups, two query tiles per workgroup)"
+    # Causal, d = 128, N >= 4096, 257-512 tiles of 128 rows: two tiles per workgroup.
+    assert fa.fa_fwd_kernel_name(1, 3, 16384, 128, True) == paired     # 384 tiles
+    assert fa.fa_fwd_kernel_name(1, 8, 8192, 128, True) == paired      # 512 tiles
+    assert fa.fa_fwd_kernel_name(1, 9, 4100, 128, True) == paired      # 297 tiles, ragged
+    assert fa.fa_fwd_kernel_name(1, 3, 16384, 128, False) == "fa_fwd_kernel"   # non-causal
+    assert fa.fa_fwd_kernel_name(1, 16, 4096, 128, True) == paired     # 512 tiles
+    assert fa.fa_fwd_kernel_name(1, 17, 4096, 128, True) == "fa_fwd_kernel"    # 544 tiles
+    assert fa.fa_fwd_kernel_name(1, 32, 2048, 128, True) == "fa_fwd_kernel"    # N < 4096
     assert fa.fa_fwd_kernel_name(1, 2, 1000, 128, True) == "fa_fwd_kernel"    # N < 1024
     assert fa.fa_fwd_kernel_name(1, 3, 16384, 64, True) == "fa_fwd_kernel"    # d = 64, 384 tiles
     assert fa.fa_fwd_kernel_name(1, 1, 16384, 64, True) == "fa_fwd_kernel (keys split between two groups)"

@@ -428,6 +428,25 @@ def test_fwd_split_key_kernel(fa, N, H, causal, scale, heads):
                        scale=scale)
 
 
+# Causal d = 128 grids of 257-512 128-row tiles with N >= 4096: the same split
+# with two query tiles per workgroup (heavy ntq-1-u, then light u). Ragged N
+# (an odd tile count leaves the middle tile alone), 297 to 512 tiles, a
+# positive non-default, a negative and a zero scale; every row of the sampled
+# heads (the first and last of each grid among them).
+@pytest.mark.parametrize("N,H,scale,heads", [
+    (4100, 9, None, [0, 4, 8]),
+    (8192, 8, None, [0, 7]),
+    (16384, 3, None, [1]),
+    (4100, 9, 0.37, [2]),
+    (4300, 12, -0.21, [11]),
+    (8192, 8, 0.0, [5]),
+])
+def test_fwd_paired_split_key_kernel(fa, N, H, scale, heads):
+    assert fa.fa_fwd_kernel_name(1, H, N, 128, True) == (
+        "fa_fwd_pp_kernel (keys split between the groups, two query tiles per workgroup)")
+    _check_fwd_sampled(fa, 1, H, N, 128, True, seed=7200 + N + H, heads=heads, scale=scale)
+
+
 # The same split at d = 64 (4-wave groups of fa_fwd_kernel in one 8-wave
 # workgroup): ragged N, both mask modes, negative and zero scales, the
 # largest such grid.
@@ -465,6 +484,7 @@ def test_fwd_split_groups_d64(fa, N, H, causal, scale, heads):
     (64, 4100, 128, False, "fa_fwd_pp_kernel", [0, 63]),
     (3, 1500, 128, True, "fa_fwd_pp_kernel (keys split", None),
     (3, 1500, 64, True, "fa_fwd_kernel (keys split", None),
+    (9, 4100, 128, True, "fa_fwd_pp_kernel (keys split between the groups, two", [0, 8]),
 ])
 def test_fwd_peaked_rows(fa, H, N, d, causal, kernel, heads, scale):
     assert fa.fa_fwd_kernel_name(1, H, N, d, causal).startswith(kernel)

@@ -64,6 +64,8 @@ def _bwd(lib, fa, q, k, v, o, do, lse, causal, scale):
     (1, 3, 1000, 64, False, "fa_fwd_kernel"),                                       # ragged, d = 64
     (1, 16, 8200, 128, True, "fa_fwd_pp_kernel"),                                   # two-group kernel
     (1, 2, 3000, 128, True, "fa_fwd_pp_kernel (keys split between the groups)"),
+    (1, 9, 4100, 128, True,
+     "fa_fwd_pp_kernel (keys split between the groups, two query tiles per workgroup)"),
     (1, 2, 3000, 64, False, "fa_fwd_kernel (keys split between two groups)"),
     (4, 33, 500, 128, True, "fa_fwd_kernel"),                                       # unsplit causal dQ
     (1, 33, 1000, 64, False, "fa_fwd_kernel"),                                      # unsplit non-causal dQ
