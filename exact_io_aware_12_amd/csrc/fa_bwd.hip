@@ -557,6 +557,10 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // g takes tiles g, g+G, ...), each with its own double buffer.
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[G][2][C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[G][2][C::TILE];
+  // With two groups (one workgroup per CU) the tile's O rows, for D, are
+  // staged in the LDS that the K / V buffers leave free.
+  __shared__ __attribute__((aligned(1024))) uint8_t o_lds[G == 2 ? 2 * C::TILE : 16];
+  static_assert(G == 1 || (2 * G * 2 + 2) * C::TILE <= 160 * 1024, "LDS");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -592,13 +596,14 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   dma_rows<D, C::LOADS>(K + off, k_lds[grp][0], min(grp, nt - 1) * C::BN, N, w, lane);
   dma_rows<D, C::LOADS>(V + off, v_lds[grp][0], min(grp, nt - 1) * C::BN, N, w, lane);
-  // The tile's Q rows (and, with two groups, its dO rows) go to LDS by
-  // coalesced copies, 64 rows per buffer, into the second buffers (free until
-  // the first step's copies): loaded one row per lane, every 16-byte load
-  // would be spread over 32 rows. Rows past N read row N-1.
+  // The tile's Q rows (and, with two groups, its dO and O rows) go to LDS by
+  // coalesced copies, 64 rows per buffer, Q and dO into the second buffers
+  // (free until the first step's copies): loaded one row per lane, every
+  // 16-byte load would be spread over 32 rows. Rows past N read row N-1.
   if constexpr (G == 2) {
     dma_rows<D, C::LOADS>(Q + off, k_lds[grp][1], q0 + 64 * grp, N, w, lane);
     dma_rows<D, C::LOADS>(dO + off, v_lds[grp][1], q0 + 64 * grp, N, w, lane);
+    dma_rows<D, C::LOADS>(O + off, o_lds + grp * C::TILE, q0 + 64 * grp, N, w, lane);
   } else {
     dma_rows<D, C::LOADS>(Q + off, k_lds[0][1], q0, N, w, lane);
     dma_rows<D, C::LOADS>(Q + off, v_lds[0][1], q0 + 64, N, w, lane);
@@ -609,15 +614,15 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // from memory), and its row statistics: LSE in log2 units and D = dO . O
   // (B1), summed over the lane's half of the row and exchanged with the
   // other half. D is also written out for the dK / dV kernel, which runs
-  // after this one. The O row chunks load meanwhile.
+  // after this one. With one group the O row chunks load meanwhile.
   bf16x8 qreg[KS], doreg[KS];
   u32x4 oreg[KS];
-  {
+  if constexpr (G == 1) {
     const size_t o = off + (size_t)qc * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       oreg[ks] = ld_global_16B(O + o + ks * 16);
-      if constexpr (G == 1) doreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(dO + o + ks * 16));
+      doreg[ks] = __builtin_bit_cast(bf16x8, ld_global_16B(dO + o + ks * 16));
     }
   }
   const float nlse2 = -LSE[(size_t)head * N + qc] * kLog2e;
@@ -742,7 +747,10 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int ks = 0; ks < KS; ++ks) {
       const int o = sw_off<RB>(row, 16 * ks + 8 * hi);
       qreg[ks] = *reinterpret_cast<const bf16x8*>(qs + o);
-      if constexpr (G == 2) doreg[ks] = *reinterpret_cast<const bf16x8*>(ds + o);
+      if constexpr (G == 2) {
+        doreg[ks] = *reinterpret_cast<const bf16x8*>(ds + o);
+        oreg[ks] = *reinterpret_cast<const u32x4*>(o_lds + h * C::TILE + o);
+      }
       const u32x4 ov = oreg[ks];
       const u32x4 dv = __builtin_bit_cast(u32x4, doreg[ks]);
 #pragma unroll
