@@ -219,13 +219,20 @@ __device__ __forceinline__ void wait_dma() {
 // exp2(s - m).
 // Item b (a workgroup, or an item of the persistent kernel) -> (head, query
 // tile rank; rank 0 = heaviest causal tile).
-__device__ __forceinline__ void item_to_tile(int b, int BH, int xcd_group, int& head, int& rank) {
+__device__ __forceinline__ void item_to_tile(int b, int BH, int xcd_group, int& head, int& rank,
+                                             int ntq = 0, bool complement = false) {
   if (xcd_group > 0) {
     // Workgroups are dispatched round-robin over the 8 XCDs; give XCD x the
     // heads [x*G, (x+1)*G) so their K/V stay in that XCD's L2.
     const int x = b & 7, s = b >> 3;
-    head = x * xcd_group + s % xcd_group;
-    rank = s / xcd_group;
+    // Item i of the XCD's heaviest-first list (heads interleaved per rank).
+    // complement: a one-round grid whose workgroups the dispatcher places
+    // breadth-first, slot 0 of the XCD's 32 CUs for s = 0..31, then slot 1
+    // for s = 32..; the second pass takes the list from its light end, so
+    // the CU holding the i-th heaviest tile also holds the i-th lightest.
+    const int i = (complement && s >= 32) ? ntq * xcd_group + 31 - s : s;
+    head = x * xcd_group + i % xcd_group;
+    rank = i / xcd_group;
   } else {
     head = b % BH;
     rank = b / BH;
@@ -560,7 +567,7 @@ template <int D, bool CAUSAL, bool POS, int G>
 __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, int BH, int N, int ntq, float c2, int xcd_group) {
+    float* __restrict__ LSE, int BH, int N, int ntq, float c2, int xcd_group, int complement) {
   using C = FwdCfg<D>;
   // Four distinct LDS objects (not one indexed array): the loop below is
   // unrolled by two so each access names its buffer statically, which lets
@@ -573,7 +580,7 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // Workgroup -> (head, query tile).
   int head, rank;
-  item_to_tile(blockIdx.x, BH, xcd_group, head, rank);
+  item_to_tile(blockIdx.x, BH, xcd_group, head, rank, ntq, complement != 0);
   fwd_tile<D, CAUSAL, POS, G>(Q, K, V, O, LSE, N, ntq, c2, head, rank, threadIdx.x, k_lds0,
                               k_lds1, v_lds0, v_lds1);
 }
@@ -684,10 +691,13 @@ static hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_
   dim3 grid((unsigned)(ntq * BH));
   if (fwd_uses_split_groups(BH, N, D)) {
     hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, POS, 2>), grid, dim3(2 * C::THREADS), 0, stream,
-                       q, k, v, o, lse, BH, N, ntq, c2, xcd_group);
+                       q, k, v, o, lse, BH, N, ntq, c2, xcd_group, 0);
   } else {
+    // Causal grids of one round (257-512 tiles, two workgroups per CU):
+    // heavy and light tiles share each CU.
+    const int complement = CAUSAL && xcd_group > 0 && ntq * BH > 256 && ntq * BH <= 512;
     hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, POS, 1>), grid, dim3(C::THREADS), 0, stream,
-                       q, k, v, o, lse, BH, N, ntq, c2, xcd_group);
+                       q, k, v, o, lse, BH, N, ntq, c2, xcd_group, complement);
   }
   return hipGetLastError();
 }
