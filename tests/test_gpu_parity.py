@@ -447,6 +447,36 @@ def test_fwd_paired_split_key_kernel(fa, N, H, scale, heads):
     _check_fwd_sampled(fa, 1, H, N, 128, True, seed=7200 + N + H, heads=heads, scale=scale)
 
 
+# Causal grids of one round (257-512 query tiles, B*H a multiple of 8) on
+# fa_fwd_kernel: the second dispatch pass takes the heaviest-first list from
+# its light end, so each CU holds a heavy and a light tile. Ragged N, a
+# partial second pass (384 tiles: 48 per XCD), d = 64, a non-default scale;
+# every row of sampled heads (each head has tiles in both passes).
+@pytest.mark.parametrize("B,H,N,d,scale,heads", [
+    (1, 16, 4000, 128, None, [0, 7, 15]),
+    (1, 24, 2000, 128, 0.37, [0, 11, 23]),
+    (3, 8, 1500, 64, None, [0, 5]),
+    (2, 16, 2048, 128, -0.21, [31]),
+])
+def test_fwd_one_round_heavy_light_pairs(fa, B, H, N, d, scale, heads):
+    assert fa.fa_fwd_kernel_name(B, H, N, d, True) == "fa_fwd_kernel"
+    tiles = (N + 127) // 128 * B * H
+    assert 256 < tiles <= 512 and (B * H) % 8 == 0
+    print(f"[fwd one-round pairs] B={B} H={H} N={N} d={d} scale={scale} heads={heads}", flush=True)
+    shape = (B, H, N, d)
+    seed = 7400 + N + H
+    qb, kb, vb = (fi.random_bf16(shape, seed + i) for i in range(3))
+    sc = 1 / math.sqrt(d) if scale is None else scale
+    o, lse, _ = _run_fwd(fa, qb, kb, vb, sc, True)
+    o_np, l_np = from_gpu(o), from_gpu(lse)
+    for flat in heads:
+        b, h = divmod(flat, H)
+        ro, rl = oracle.attention_fwd(bits_to_f64(qb[b, h]), bits_to_f64(kb[b, h]),
+                                      bits_to_f64(vb[b, h]), sc, True)
+        assert_close(f"O[{b},{h}]", o_np[b, h], ro, TOL_O)
+        assert_close(f"LSE[{b},{h}]", l_np[b, h], rl, TOL_LSE)
+
+
 # The same split at d = 64 (4-wave groups of fa_fwd_kernel in one 8-wave
 # workgroup): ragged N, both mask modes, negative and zero scales, the
 # largest such grid.
