@@ -26,6 +26,9 @@
 //          wave); R = 2 at one wave per SIMD is a 64-row-per-wave design
 //          (twice the output registers, so one wave per SIMD), which halves
 //          the LDS bytes per MFMA
+//   hbm    streaming reads of a 2 GiB buffer (global_load_dwordx4, grid
+//          stride, U loads in flight per lane, plain or non-temporal), the
+//          practical read ceiling of the HBM-bound decode kernel
 //
 // Each is timed with HIP events at one and two 4-wave workgroups per CU (one
 // and two waves per SIMD), on 256 x {1,2} workgroups. Every kernel writes one
@@ -299,6 +302,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+template <int U, bool NT>
+__global__ __launch_bounds__(256) void k_hbm(const u32x4* __restrict__ src, size_t n16, unsigned* out) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + (size_t)(U - 1) * stride < n16; i += (size_t)U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(src + i + u * stride) : src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  for (; i < n16; i += stride) acc ^= src[i];
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 // Milliseconds of one launch after a short warm-up launch.
 template <typename F>
 static int timed(F launch, hipEvent_t e0, hipEvent_t e1, float* ms) {
@@ -381,6 +401,21 @@ int main() {
     }
     FA_FULL(1, 2) FA_FULL(2, 1) FA_FULL(1, 1) FA_FULL(2, 2)
 #undef FA_FULL
+  }
+  // Streaming HBM reads (one launch reads the whole buffer; its contents do
+  // not matter). out2 holds one word per thread of the largest grid.
+  {
+    const size_t bytes = (size_t)2 << 30, n16 = bytes / 16;
+    u32x4* buf = nullptr;
+    unsigned* out2 = nullptr;
+    CHECK(hipMalloc(&buf, bytes));
+    CHECK(hipMalloc(&out2, (size_t)8192 * 256 * sizeof(unsigned)));
+    float ms = 0.f;
+#define FA_HBM(U, NT)                                                                                   for (int nb = 1024; nb <= 8192; nb *= 2) {                                                            if (timed([&](bool) { hipLaunchKernelGGL((k_hbm<U, NT>), dim3(nb), dim3(256), 0, 0, buf, n16, out2); }, e0, e1, &ms)) return 1;       printf("| HBM read, global_load_dwordx4, %d in flight per lane%s, %d workgroups of 4 waves | %d | %.2f TB/s | |\n", U, NT ? ", non-temporal" : "", nb, nb / 256, bytes / (ms * 1e-3) / 1e12);     }
+    FA_HBM(4, false) FA_HBM(8, false) FA_HBM(4, true) FA_HBM(8, true)
+#undef FA_HBM
+    CHECK(hipFree(out2));
+    CHECK(hipFree(buf));
   }
   CHECK(hipFree(out));
   return 0;
