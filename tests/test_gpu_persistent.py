@@ -66,6 +66,12 @@ def test_persistent_matches_oracle(fa, B, H, N, d, causal, scale):
     (2, 32, 4096, 128, True),     # the causal workload-3 shape: 2048 items, 4 per workgroup
     (1, 5, 16400, 64, True),      # 645 items, heads not grouped by XCD
     (4, 16, 2000, 128, False),    # 1024 items
+    # One-round causal grids, where fa_fwd places a heavy and a light tile on
+    # each CU (the dispatch order differs from the comparator's): every tile
+    # of every head must still be computed exactly once.
+    (2, 16, 2048, 128, True),     # 512 items
+    (1, 24, 2000, 128, True),     # 384 items: a partial second pass
+    (3, 8, 1500, 64, True),       # 288 items, d = 64
 ])
 def test_persistent_equals_fused_forward(fa, B, H, N, d, causal):
     import torch
