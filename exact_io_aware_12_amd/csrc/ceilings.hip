@@ -29,6 +29,16 @@
 //   hbm    streaming reads of a 2 GiB buffer (global_load_dwordx4, grid
 //          stride, U loads in flight per lane, plain or non-temporal), the
 //          practical read ceiling of the HBM-bound decode kernel
+//   dqacc  fp32 adds into a dQ-shaped accumulator (32 heads x 2048 rows x
+//          128 columns) in the pattern a fused dK/dV/dQ kernel would use at
+//          B=2, H=16, N=2048, causal: 256 workgroups of 8 waves, each a pair
+//          of 128-key tiles (u, 15-u) walking its 34 query tiles of 64 rows and
+//          adding one 64 x 128 block per tile (32 lanes of a wave cover 128
+//          contiguous bytes of a row). Plain stores of the same blocks
+//          against global_atomic_add_f32 at agent and at workgroup scope
+//          (the two scopes give the same instruction here). The workgroups of
+//          one head sit on one XCD under round-robin placement. Every element
+//          of the accumulator is checked against its exact count
 //
 // Each is timed with HIP events at one and two 4-wave workgroups per CU (one
 // and two waves per SIMD), on 256 x {1,2} workgroups. Every kernel writes one
@@ -39,6 +49,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 #include <hip/hip_runtime.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -319,6 +330,34 @@ __global__ __launch_bounds__(256) void k_hbm(const u32x4* __restrict__ src, size
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// One block of the dQ-shaped accumulator per (workgroup, query tile): a
+// workgroup is a causal pair of 128-key tiles (u, 15 - u) of one head and
+// adds into the 64-row query tiles 2*kt .. 31 of each (34 in all). Wave w
+// covers rows 32*(w/4) .. +32 and columns 32*(w%4) .. +32 of the block in the
+// layout of a 32x32 MFMA accumulator (lane -> column). Heads 4x .. 4x+3 go to
+// workgroups b with b % 8 == x. Indexes stay inside 32 x 2048 x 128.
+template <int MODE>
+__global__ __launch_bounds__(512) void k_dqacc(float* __restrict__ acc) {
+  const int b = blockIdx.x, slot = b / 8;
+  const int head = (b % 8) * 4 + slot % 4, u = slot / 4;
+  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+  float* hp = acc + (size_t)head * 2048 * 128;
+  const int col = 32 * (w % 4) + lane % 32;
+  for (int part = 0; part < 2; ++part) {
+    const int kt = part == 0 ? u : 15 - u;
+    for (int qt = 2 * kt; qt < 32; ++qt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 64 * qt + 32 * (w / 4) + 8 * (i / 4) + 4 * (lane / 32) + i % 4;
+        float* p = hp + (size_t)row * 128 + col;
+        if constexpr (MODE == 0) *p = 1.0f;
+        else if constexpr (MODE == 1) __hip_atomic_fetch_add(p, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else __hip_atomic_fetch_add(p, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+  }
+}
+
 // Milliseconds of one launch after a short warm-up launch.
 template <typename F>
 static int timed(F launch, hipEvent_t e0, hipEvent_t e1, float* ms) {
@@ -416,6 +455,44 @@ int main() {
 #undef FA_HBM
     CHECK(hipFree(out2));
     CHECK(hipFree(buf));
+  }
+  // fp32 adds into a dQ-shaped accumulator (best of 3 launches, each on a
+  // zeroed buffer; every element checked against its exact count).
+  {
+    const size_t n = (size_t)32 * 2048 * 128;
+    float* acc = nullptr;
+    CHECK(hipMalloc(&acc, n * sizeof(float)));
+    float* host = (float*)malloc(n * sizeof(float));
+    if (!host) return 1;
+    const double bytes = 256.0 * 34 * 64 * 128 * 4;
+    for (int mode = 0; mode < 3; ++mode) {
+      float best = 1e30f;
+      for (int t = 0; t < 3; ++t) {
+        CHECK(hipMemset(acc, 0, n * sizeof(float)));
+        CHECK(hipDeviceSynchronize());
+        CHECK(hipEventRecord(e0));
+        if (mode == 0) hipLaunchKernelGGL(k_dqacc<0>, dim3(256), dim3(512), 0, 0, acc);
+        if (mode == 1) hipLaunchKernelGGL(k_dqacc<1>, dim3(256), dim3(512), 0, 0, acc);
+        if (mode == 2) hipLaunchKernelGGL(k_dqacc<2>, dim3(256), dim3(512), 0, 0, acc);
+        CHECK(hipGetLastError());
+        CHECK(hipEventRecord(e1));
+        CHECK(hipEventSynchronize(e1));
+        float ms = 0.f;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        if (ms < best) best = ms;
+      }
+      CHECK(hipMemcpy(host, acc, n * sizeof(float), hipMemcpyDeviceToHost));
+      long bad = 0;
+      for (size_t e = 0; e < n; ++e) {
+        const int qt = (int)((e / 128) % 2048) / 64;
+        if (host[e] != (mode == 0 ? 1.0f : (float)(qt / 2 + 1))) ++bad;
+      }
+      printf("| dQ-shaped accumulator, %s, %.1f MB per launch | 1 (8 waves) | %.2f TB/s (%.1f us) | %ld wrong elements |\n",
+             mode == 0 ? "plain stores" : mode == 1 ? "global_atomic_add_f32, agent scope" : "global_atomic_add_f32, workgroup scope",
+             bytes / 1e6, bytes / (best * 1e-3) / 1e12, best * 1e3, bad);
+    }
+    free(host);
+    CHECK(hipFree(acc));
   }
   CHECK(hipFree(out));
   return 0;
