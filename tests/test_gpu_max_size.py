@@ -87,3 +87,32 @@ def test_max_size_fwd_bwd(fa, B, H, N, d, causal):
         assert_close(f"LSE[{h}]", got["LSE"], rl[m], TOL_LSE)
         for i, name in enumerate(("dQ", "dK", "dV")):
             assert_close(f"{name}[{h}]", got[name], rg[m][i], TOL_GRAD)
+
+
+# Decode at the largest single-head cache: Nk = 2^24 - 1 keys at d = 128 and
+# 2^25 - 1 at d = 64 (4 GiB per K and V tensor), so the key offsets within
+# one head reach 4 GiB. The cache repeats a seeded block of pk keys c times
+# (Nk = c * pk). Every distinct key then carries c times the weight of its
+# single copy, so the softmax weights of the block, and O, are unchanged, and
+# the LSE is the block's plus ln c: the oracle computes the block's O and LSE.
+@pytest.mark.parametrize("d,pk", [(128, 255), (64, 601)])
+def test_max_size_decode(fa, d, pk):
+    import torch
+    nk = (2**31 - 1) // d
+    assert nk % pk == 0 and nk * d > 2**31 - 1 - d
+    c, nq = nk // pk, 8
+    print(f"[max size decode] Nq={nq} Nk={nk} d={d} block={pk} copies={c}", flush=True)
+    seed = 32000 + d
+    qb = fi.random_bf16((1, 1, nq, d), seed)
+    kb = fi.random_bf16((1, 1, pk, d), seed + 1)
+    vb = fi.random_bf16((1, 1, pk, d), seed + 2)
+    idx = torch.arange(nk, device="cuda") % pk
+    k = to_gpu_bf16(kb)[:, :, idx]
+    v = to_gpu_bf16(vb)[:, :, idx]
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.decode_fwd(to_gpu_bf16(qb), k, v, causal=False, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_decode(bits_to_f64(qb), bits_to_f64(kb), bits_to_f64(vb), scale,
+                                     False)
+    assert_close("O", from_gpu(o), ro, TOL_O)
+    assert_close("LSE", from_gpu(lse), rl + math.log(c), TOL_LSE)
