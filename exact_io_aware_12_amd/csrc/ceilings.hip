@@ -26,6 +26,11 @@
 //          wave); R = 2 at one wave per SIMD is a 64-row-per-wave design
 //          (twice the output registers, so one wave per SIMD), which halves
 //          the LDS bytes per MFMA
+//   ldsclk LDS read rate per CU per actual shader clock: one workgroup of
+//          4, 8 or 16 waves per CU, R independent reads per lane in flight
+//          (ds_read_b128, or ds_read_b64_tr_b16), lane-contiguous 16-byte
+//          chunks of a 32 KiB tile; the clock comes from s_memtime against
+//          s_memrealtime (100 MHz) between two barriers inside each workgroup
 //   hbm    streaming reads of a 2 GiB buffer (global_load_dwordx4, grid
 //          stride, U loads in flight per lane, plain or non-temporal), the
 //          practical read ceiling of the HBM-bound decode kernel
@@ -54,6 +59,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -330,6 +336,44 @@ __global__ __launch_bounds__(256) void k_hbm(const u32x4* __restrict__ src, size
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// LDS reads for the per-clock rate (see the header): clk[2b] and clk[2b+1]
+// are workgroup b's s_memtime and s_memrealtime deltas between the barriers.
+// Indexes stay inside the 32 KiB tile (masked to 2047 chunks).
+template <int NT, int R, bool TR>
+__global__ __launch_bounds__(NT) void k_ldsclk(unsigned* out, long long* clk, int iters) {
+  __shared__ u32x4 buf[2048];
+  for (int i = threadIdx.x; i < 2048; i += NT) buf[i] = u32x4{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
+  u32x4 acc = {0, 0, 0, 0};
+  int idx = threadIdx.x & 2047;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = (idx + r * 64) & 2047;
+      if constexpr (TR) {
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS s16x4*)((LDS_AS char*)(LDS_AS void*)buf + c * 16));
+        const u32x2 u = __builtin_bit_cast(u32x2, v);
+        acc[2 * (r & 1)] ^= u[0];
+        acc[2 * (r & 1) + 1] ^= u[1];
+      } else {
+        acc ^= buf[c];
+      }
+    }
+    idx = (idx + 7) & 2047;
+  }
+  out[blockIdx.x * NT + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  __syncthreads();
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  const long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    clk[2 * blockIdx.x] = t1 - t0;
+    clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 // One block of the dQ-shaped accumulator per (workgroup, query tile): a
 // workgroup is a causal pair of 128-key tiles (u, 15 - u) of one head and
 // adds into the 64-row query tiles 2*kt .. 31 of each (34 in all). Wave w
@@ -455,6 +499,32 @@ int main() {
 #undef FA_HBM
     CHECK(hipFree(out2));
     CHECK(hipFree(buf));
+  }
+  // LDS read rate per CU per actual clock (one workgroup per CU, 256 CUs).
+  {
+    unsigned* o3 = nullptr;
+    long long* ck = nullptr;
+    CHECK(hipMalloc(&o3, 256 * 1024 * sizeof(unsigned)));
+    CHECK(hipMalloc(&ck, 2 * 256 * sizeof(long long)));
+    long long hk[512];
+    printf("| LDS read | waves per CU | reads in flight per lane | rate (all CUs) | per CU per actual clock |\n|---|---|---|---|---|\n");
+#define FA_LDSCLK(NT, R, TR)                                                                        \
+    {                                                                                               \
+      const int it = 4000;                                                                          \
+      float ms = 0.f;                                                                               \
+      if (timed([&](bool w) { hipLaunchKernelGGL((k_ldsclk<NT, R, TR>), dim3(256), dim3(NT), 0, 0, o3, ck, w ? 10 : it); }, e0, e1, &ms)) return 1; \
+      CHECK(hipMemcpy(hk, ck, sizeof(hk), hipMemcpyDeviceToHost));                                  \
+      double mc = 0, mr = 0;                                                                        \
+      for (int i = 0; i < 256; ++i) { mc += (double)hk[2 * i]; mr += (double)hk[2 * i + 1]; }       \
+      const double bytes = (double)NT * it * R * (TR ? 8 : 16);                                     \
+      printf("| %s | %d | %d | %.1f TB/s | %.0f B (clock %.0f MHz) |\n", TR ? "ds_read_b64_tr_b16" : "ds_read_b128", \
+             NT / 64, R, 256.0 * bytes / (ms * 1e-3) / 1e12, bytes * 256 / mc, mc / mr * 100.0);     \
+    }
+    FA_LDSCLK(256, 16, false) FA_LDSCLK(512, 16, false) FA_LDSCLK(1024, 16, false)
+    FA_LDSCLK(512, 16, true) FA_LDSCLK(1024, 16, true)
+#undef FA_LDSCLK
+    CHECK(hipFree(ck));
+    CHECK(hipFree(o3));
   }
   // fp32 adds into a dQ-shaped accumulator (best of 3 launches, each on a
   // zeroed buffer; every element checked against its exact count).
